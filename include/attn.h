@@ -1,0 +1,120 @@
+/*
+ * attn.h -- C ABI of the gfx950 FlashAttention forward library (libattn.so).
+ *
+ * What is computed.  Per (batch b, query head hq), with kv head
+ * hkv = hq / (Hq / Hkv) (contiguous groups of query heads share one K/V head):
+ *
+ *     O[i,:] = sum_j softmax_j( scale * q_i . k_j  [+ causal mask] ) v_j
+ *     LSE[i] = ln sum_{visible j} exp(scale * q_i . k_j)
+ *
+ * computed with an online softmax whose running max and sum are carried across
+ * key tiles, so the score matrix never leaves the chip ("The FA5090
+ * Optimization Journey", sec. 2.2 and 2.6; "10 rounds of hand-written fused
+ * attention ...", "The trajectory", round R8).  Inputs are IEEE binary16 or
+ * bfloat16; products accumulate in fp32; O has the input dtype; LSE is fp32.
+ *
+ * Causal masking: key j is visible to query i iff j <= i + (Sk - Sq)
+ * (bottom-right aligned; j <= i when Sq == Sk).  A query row that sees no key
+ * gets O = 0 and LSE = -inf.
+ *
+ * Layout.  Every tensor is contiguous row-major with d innermost:
+ *     q, o: [B, Hq, Sq, d]      k, v: [B, Hkv, Sk, d]      lse: [B, Hq, Sq]
+ * All data pointers are device pointers, 16-byte aligned, owned by the caller.
+ * The library allocates nothing and keeps no state between calls.
+ *
+ * Streams.  Work is enqueued on `stream` (a hipStream_t; NULL = the default
+ * stream) and the call returns before it completes.  Concurrent calls on
+ * different streams are independent.
+ *
+ * Errors.  Arguments are validated before any HIP call; a failing check
+ * returns its status and enqueues nothing.  A HIP launch error returns
+ * ATTN_ERR_HIP.  attn_last_error() then describes the failure (thread-local).
+ * The library never aborts, exits or throws across this interface.
+ */
+#ifndef ATTN_H
+#define ATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { ATTN_F16 = 0, ATTN_BF16 = 1 } attn_dtype;
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL = 1,        /* a required pointer is NULL */
+  ATTN_ERR_SHAPE = 2,       /* non-positive size, Hq % Hkv != 0, size overflow */
+  ATTN_ERR_UNSUPPORTED = 3, /* valid but not implemented: d != 128, dtype, GQA group > 32 */
+  ATTN_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
+  ATTN_ERR_WORKSPACE = 5,   /* decode workspace missing or too small */
+  ATTN_ERR_NO_DEVICE = 6,   /* no HIP device visible */
+  ATTN_ERR_HIP = 7,         /* a HIP call failed; see attn_last_error() */
+  ATTN_ERR_VALUE = 8        /* bad scalar: causal not 0/1, scale negative or not finite,
+                               num_splits out of range */
+} attn_status;
+
+/*
+ * Prefill / full forward pass.
+ *   q, k, v  : inputs (dtype given by `dtype`), layouts above.
+ *   o        : output [B,Hq,Sq,d], same dtype as the inputs.
+ *   lse      : fp32 [B,Hq,Sq] natural-log LSE of the scaled scores over the
+ *              visible keys; may be NULL when not wanted.
+ *   scale    : multiplies q.k before the softmax (usually 1/sqrt(d)); >= 0.
+ *   causal   : 0 or 1.
+ *   d        : head dimension; 128 is implemented.
+ * The exponentials run in base 2 with scale*log2(e) folded into one multiply
+ * ("The FA5090 Optimization Journey", sec. 2.6; "G5: Pipeline ...", V33).
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int Hq, int Hkv, int Sq, int Sk, int d, int causal, float scale,
+             int dtype, void* stream);
+
+/*
+ * Bytes of device workspace attn_fwd_decode needs: fp32 partial outputs
+ * [B,Hq,num_splits,d] followed (256-byte aligned) by fp32 partial LSEs
+ * [B,Hq,num_splits].  Returns 0 for invalid arguments.
+ */
+size_t attn_decode_workspace_bytes(int B, int Hq, int d, int num_splits);
+
+/*
+ * Single-token decode with split-KV: the same result as attn_fwd with Sq = 1
+ * and causal = 0, computed by cutting the Sk keys into num_splits consecutive
+ * chunks of ceil(Sk/num_splits) keys, attending to each chunk independently
+ * (one read of each K/V row serves all Hq/Hkv query heads of its group), and
+ * merging the partial results by their LSEs (attn_splitkv_combine).  Split-KV
+ * as a way to spread one row's keys over more of the chip: "The FA5090
+ * Optimization Journey", sec. 2.7.
+ *   q, o     : [B,Hq,1,d]; k, v: [B,Hkv,Sk,d]; lse: fp32 [B,Hq] or NULL.
+ *   num_splits in [1, Sk]; Hq/Hkv <= 32.
+ *   workspace: device buffer of at least attn_decode_workspace_bytes(...)
+ *              bytes, owned by the caller; its contents on entry are ignored.
+ * Enqueues the split kernel, then the combine kernel, on `stream`.
+ */
+int attn_fwd_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int B, int Hq, int Hkv, int Sk, int d, float scale, int dtype,
+                    int num_splits, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Merge split partials: for each of the B*Hq rows,
+ *     M = max_s lse_s,  w_s = exp(lse_s - M),  L = sum_s w_s,
+ *     O = sum_s (w_s / L) o_s  (rounded to dtype),  LSE = M + ln L.
+ * A row whose partial LSEs are all -inf gets O = 0 and LSE = -inf.  This is the
+ * online-softmax merge of two running states applied across splits ("The FA5090
+ * Optimization Journey", sec. 2.6, the running max and the final 1/l).
+ *   o_part  : fp32 [B,Hq,num_splits,d], each partial already normalised.
+ *   lse_part: fp32 [B,Hq,num_splits], natural log.
+ *   o       : [B,Hq,d] in dtype;  lse: fp32 [B,Hq] or NULL.
+ */
+int attn_splitkv_combine(const float* o_part, const float* lse_part, void* o, float* lse,
+                         int B, int Hq, int d, int num_splits, int dtype, void* stream);
+
+/* Description of the last non-OK status returned on this thread ("" if none). */
+const char* attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H */
