@@ -1,1 +1,187 @@
-"""gfx950 FlashAttention forward: Python binding of libattn.so (placeholder until the HIP library lands)."""
+"""gfx950 FlashAttention forward -- Python binding of libattn.so.
+
+The binding only marshals arguments: it takes device pointers and the current
+torch stream from torch tensors and calls the C ABI declared in
+``include/attn.h``.  Every step of the computation runs in the library's HIP
+kernels; there is no fallback.  When libattn.so is missing (not built) any call
+raises, naming the build command.
+
+    from attention_forward_amd import attn_fwd
+    o, lse = attn_fwd(q, k, v, causal=True)          # q [B,Hq,Sq,d], k/v [B,Hkv,Sk,d]
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libattn.so")
+
+# status codes (include/attn.h)
+ATTN_OK = 0
+ATTN_ERR_NULL = 1
+ATTN_ERR_SHAPE = 2
+ATTN_ERR_UNSUPPORTED = 3
+ATTN_ERR_ALIGN = 4
+ATTN_ERR_WORKSPACE = 5
+ATTN_ERR_NO_DEVICE = 6
+ATTN_ERR_HIP = 7
+ATTN_ERR_VALUE = 8
+ATTN_F16 = 0
+ATTN_BF16 = 1
+
+EXPORTED = ("attn_fwd", "attn_decode_workspace_bytes", "attn_fwd_decode", "attn_splitkv_combine",
+            "attn_last_error")
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__("attn status %d: %s" % (status, message))
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libattn.so (raises if it was never built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libattn.so is not built; run `python -m attention_forward_amd.build` "
+                          "(or __graft_entry__.build())")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    L.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp]
+    L.attn_fwd.restype = i
+    L.attn_decode_workspace_bytes.argtypes = [i, i, i, i]
+    L.attn_decode_workspace_bytes.restype = sz
+    L.attn_fwd_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, sz, vp]
+    L.attn_fwd_decode.restype = i
+    L.attn_splitkv_combine.argtypes = [vp, vp, vp, vp, i, i, i, i, i, vp]
+    L.attn_splitkv_combine.restype = i
+    L.attn_last_error.argtypes = []
+    L.attn_last_error.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def last_error() -> str:
+    return lib().attn_last_error().decode()
+
+
+def _check(status: int):
+    if status != ATTN_OK:
+        raise AttnError(status, last_error())
+
+
+def _dtype_code(t) -> int:
+    import torch
+
+    if t.dtype == torch.float16:
+        return ATTN_F16
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    raise AttnError(ATTN_ERR_UNSUPPORTED, "dtype %s (fp16 or bf16 only)" % t.dtype)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    import torch
+
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _require(t, name):
+    if not t.is_cuda:
+        raise AttnError(ATTN_ERR_VALUE, "%s must be a device tensor" % name)
+    if not t.is_contiguous():
+        raise AttnError(ATTN_ERR_VALUE, "%s must be contiguous" % name)
+
+
+def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None,
+             want_lse: bool = True):
+    """O = softmax(scale * Q K^T [causal]) V per (batch, head); returns (o, lse).
+
+    q [B,Hq,Sq,d], k and v [B,Hkv,Sk,d], contiguous fp16/bf16 device tensors.
+    lse is fp32 [B,Hq,Sq] (None when want_lse is False).  Runs on the current
+    torch stream; returns without waiting for the kernel.
+    """
+    import torch
+
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _require(t, nm)
+    B, Hq, Sq, d = q.shape
+    Bk, Hkv, Sk, dk = k.shape
+    if Bk != B or dk != d or tuple(v.shape) != tuple(k.shape):
+        raise AttnError(ATTN_ERR_SHAPE, "q %s / k %s / v %s shapes disagree"
+                        % (tuple(q.shape), tuple(k.shape), tuple(v.shape)))
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise AttnError(ATTN_ERR_UNSUPPORTED, "q, k, v must share one dtype")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    st = lib().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Sq, Sk, d,
+                        1 if causal else 0, float(scale), _dtype_code(q), _stream(q.device))
+    _check(st)
+    return out, lse
+
+
+def attn_decode_workspace_bytes(B: int, Hq: int, d: int, num_splits: int) -> int:
+    return int(lib().attn_decode_workspace_bytes(B, Hq, d, num_splits))
+
+
+def attn_fwd_decode(q, k, v, num_splits: int, scale: float | None = None, out=None, lse=None,
+                    workspace=None, want_lse: bool = True):
+    """Single-token decode with split-KV; q [B,Hq,1,d], k/v [B,Hkv,Sk,d].
+
+    Returns (o [B,Hq,1,d], lse [B,Hq] fp32).  `workspace` (uint8 device tensor
+    of at least attn_decode_workspace_bytes bytes) is allocated when omitted.
+    """
+    import torch
+
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _require(t, nm)
+    B, Hq, Sq, d = q.shape
+    if Sq != 1:
+        raise AttnError(ATTN_ERR_SHAPE, "decode takes one query row (Sq = 1), got %d" % Sq)
+    _, Hkv, Sk, _ = k.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = attn_decode_workspace_bytes(B, Hq, d, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    st = lib().attn_fwd_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Sk, d,
+                               float(scale), _dtype_code(q), int(num_splits), _ptr(workspace),
+                               workspace.numel() * workspace.element_size(), _stream(q.device))
+    _check(st)
+    return out, lse
+
+
+def attn_splitkv_combine(o_part, lse_part, dtype, out=None, lse=None, want_lse: bool = True):
+    """Merge fp32 partials o_part [B,Hq,S,d] / lse_part [B,Hq,S] -> (o [B,Hq,d], lse [B,Hq])."""
+    import torch
+
+    _require(o_part, "o_part")
+    _require(lse_part, "lse_part")
+    B, Hq, S, d = o_part.shape
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=dtype, device=o_part.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=o_part.device)
+    code = ATTN_F16 if dtype == torch.float16 else ATTN_BF16 if dtype == torch.bfloat16 else -1
+    st = lib().attn_splitkv_combine(_ptr(o_part), _ptr(lse_part), _ptr(out), _ptr(lse), B, Hq, d,
+                                    S, code, _stream(o_part.device))
+    _check(st)
+    return out, lse

@@ -1,0 +1,158 @@
+// C ABI of libattn.so (declared in include/attn.h): argument validation, the
+// thread-local error message, and dispatch to the kernel launchers.  Every
+// check runs before the first HIP call, so a rejected call enqueues nothing.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+
+#include "attn.h"
+#include "launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+int check_device() {
+  int n = 0;
+  hipError_t e = hipGetDeviceCount(&n);
+  if (e != hipSuccess || n <= 0)
+    return fail(ATTN_ERR_NO_DEVICE, "no HIP device visible (%s)", hipGetErrorString(e));
+  return ATTN_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ATTN_OK;
+  return fail(ATTN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+float fold_log2e(float scale) { return (float)((double)scale * 1.4426950408889634074); }
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_last_error(void) { return g_err; }
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+             int Hkv, int Sq, int Sk, int d, int causal, float scale, int dtype, void* stream) {
+  g_err[0] = '\0';
+  if (!q || !k || !v || !o) return fail(ATTN_ERR_NULL, "attn_fwd: q, k, v and o must be non-NULL");
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Sq <= 0 || Sk <= 0 || d <= 0)
+    return fail(ATTN_ERR_SHAPE, "attn_fwd: sizes must be positive (B=%d Hq=%d Hkv=%d Sq=%d Sk=%d d=%d)",
+                B, Hq, Hkv, Sq, Sk, d);
+  if (Hq % Hkv != 0)
+    return fail(ATTN_ERR_SHAPE, "attn_fwd: Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  if (dtype != ATTN_F16 && dtype != ATTN_BF16)
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd: dtype %d is not 0 (fp16) or 1 (bf16)", dtype);
+  if (d != attn::HEAD_DIM) return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd: head dim %d (only 128)", d);
+  if (causal != 0 && causal != 1) return fail(ATTN_ERR_VALUE, "attn_fwd: causal must be 0 or 1");
+  if (!std::isfinite(scale) || scale < 0.0f)
+    return fail(ATTN_ERR_VALUE, "attn_fwd: scale must be finite and >= 0");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+      (lse && !aligned4(lse)))
+    return fail(ATTN_ERR_ALIGN, "attn_fwd: q, k, v, o must be 16-byte aligned, lse 4-byte");
+  const long long items = (long long)B * Hq * ((Sq + attn::FWD_BR - 1) / attn::FWD_BR);
+  const long long q_elems = (long long)B * Hq * Sq * d;
+  const long long kv_elems = (long long)B * Hkv * Sk * d;
+  if (items > INT_MAX || q_elems > (1LL << 46) || kv_elems > (1LL << 46))
+    return fail(ATTN_ERR_SHAPE, "attn_fwd: problem too large for one launch");
+  int st = check_device();
+  if (st != ATTN_OK) return st;
+  attn::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, causal, fold_log2e(scale), dtype};
+  return hip_status(attn::launch_fwd(a, static_cast<hipStream_t>(stream)), "attn_fwd launch");
+}
+
+size_t attn_decode_workspace_bytes(int B, int Hq, int d, int num_splits) {
+  if (B <= 0 || Hq <= 0 || d <= 0 || num_splits <= 0) return 0;
+  const size_t rows = (size_t)B * Hq * num_splits;
+  return round_up(rows * d * sizeof(float)) + round_up(rows * sizeof(float));
+}
+
+int attn_splitkv_combine(const float* o_part, const float* lse_part, void* o, float* lse, int B,
+                         int Hq, int d, int num_splits, int dtype, void* stream) {
+  g_err[0] = '\0';
+  if (!o_part || !lse_part || !o)
+    return fail(ATTN_ERR_NULL, "attn_splitkv_combine: o_part, lse_part and o must be non-NULL");
+  if (B <= 0 || Hq <= 0 || d <= 0)
+    return fail(ATTN_ERR_SHAPE, "attn_splitkv_combine: sizes must be positive");
+  if (num_splits <= 0) return fail(ATTN_ERR_VALUE, "attn_splitkv_combine: num_splits must be >= 1");
+  if (dtype != ATTN_F16 && dtype != ATTN_BF16)
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_splitkv_combine: dtype %d", dtype);
+  if (d != attn::HEAD_DIM)
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_splitkv_combine: head dim %d (only 128)", d);
+  if (!aligned16(o_part) || !aligned4(lse_part) || !aligned16(o) || (lse && !aligned4(lse)))
+    return fail(ATTN_ERR_ALIGN, "attn_splitkv_combine: misaligned pointer");
+  if ((long long)B * Hq > INT_MAX)
+    return fail(ATTN_ERR_SHAPE, "attn_splitkv_combine: too many rows");
+  int st = check_device();
+  if (st != ATTN_OK) return st;
+  attn::CombineArgs a{o_part, lse_part, o, lse, B * Hq, num_splits, dtype};
+  return hip_status(attn::launch_combine(a, static_cast<hipStream_t>(stream)),
+                    "attn_splitkv_combine launch");
+}
+
+int attn_fwd_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                    int Hq, int Hkv, int Sk, int d, float scale, int dtype, int num_splits,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = '\0';
+  if (!q || !k || !v || !o)
+    return fail(ATTN_ERR_NULL, "attn_fwd_decode: q, k, v and o must be non-NULL");
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Sk <= 0 || d <= 0)
+    return fail(ATTN_ERR_SHAPE, "attn_fwd_decode: sizes must be positive");
+  if (Hq % Hkv != 0)
+    return fail(ATTN_ERR_SHAPE, "attn_fwd_decode: Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  if (dtype != ATTN_F16 && dtype != ATTN_BF16)
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd_decode: dtype %d", dtype);
+  if (d != attn::HEAD_DIM) return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd_decode: head dim %d (only 128)", d);
+  if (Hq / Hkv > 32)
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd_decode: query heads per kv head %d > 32",
+                Hq / Hkv);
+  if (num_splits < 1 || num_splits > Sk)
+    return fail(ATTN_ERR_VALUE, "attn_fwd_decode: num_splits=%d not in [1, Sk=%d]", num_splits, Sk);
+  if (!std::isfinite(scale) || scale < 0.0f)
+    return fail(ATTN_ERR_VALUE, "attn_fwd_decode: scale must be finite and >= 0");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+      (lse && !aligned4(lse)))
+    return fail(ATTN_ERR_ALIGN, "attn_fwd_decode: q, k, v, o must be 16-byte aligned, lse 4-byte");
+  const size_t need = attn_decode_workspace_bytes(B, Hq, d, num_splits);
+  if (!workspace || workspace_bytes < need)
+    return fail(ATTN_ERR_WORKSPACE, "attn_fwd_decode: workspace of %zu bytes needed, %zu given",
+                need, workspace ? workspace_bytes : (size_t)0);
+  if (!aligned16(workspace)) return fail(ATTN_ERR_ALIGN, "attn_fwd_decode: misaligned workspace");
+  if ((long long)B * Hkv * num_splits > INT_MAX || (long long)B * Hq > INT_MAX ||
+      (long long)B * Hkv * Sk * d > (1LL << 46))
+    return fail(ATTN_ERR_SHAPE, "attn_fwd_decode: problem too large for one launch");
+  int st = check_device();
+  if (st != ATTN_OK) return st;
+  const size_t rows = (size_t)B * Hq * num_splits;
+  float* o_part = static_cast<float*>(workspace);
+  float* lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                             round_up(rows * d * sizeof(float)));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  attn::DecodeArgs da{q, k, v, o_part, lse_part, B, Hq, Hkv, Sk, num_splits, fold_log2e(scale),
+                      dtype};
+  st = hip_status(attn::launch_decode_split(da, s), "attn_fwd_decode split launch");
+  if (st != ATTN_OK) return st;
+  attn::CombineArgs ca{o_part, lse_part, o, lse, B * Hq, num_splits, dtype};
+  return hip_status(attn::launch_combine(ca, s), "attn_fwd_decode combine launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,153 @@
+// Single-token decode with split-KV, and the LSE merge of the split partials.
+//
+// Split kernel: one single-wave workgroup per (batch, kv head, split).  The 32
+// query slots of the MFMA tile hold the query heads of the kv head's group (up
+// to 32), so each K/V row is read from HBM once for the whole group; the rest
+// of the slots are zero and never stored.  The split's keys stream through a
+// 32 KiB LDS stage (K and V of 64 keys), which lets five such workgroups share
+// a CU and keeps enough bytes in flight for the HBM-bound loop (a
+// matrix-vector product has an arithmetic intensity near 1 FLOP/B, "The FA5090
+// Optimization Journey", sec. 2.3).  The partial output is normalised by its
+// own sum and stored in fp32 with its natural-log LSE.
+//
+// Combine kernel: per (batch, query head), the partials are merged by their
+// LSEs, which is the online-softmax rescale of the running state applied across
+// splits instead of across tiles ("The FA5090 Optimization Journey", sec. 2.6).
+#include "fa_common.h"
+#include "launch.h"
+
+namespace attn {
+
+template <int DT>
+__global__ __launch_bounds__(64, 2) void fa_decode_split_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, float* __restrict__ o_part, float* __restrict__ lse_part,
+    int Hq, int Hkv, int Sk, int num_splits, float scale_log2) {
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * TILE_BYTES];
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 5;
+  const int n = lane & 31;
+
+  const int t = blockIdx.x;
+  const int split = t % num_splits;
+  const int bk = t / num_splits;  // b * Hkv + hkv
+  const int b = bk / Hkv;
+  const int hkv = bk - b * Hkv;
+  const int G = Hq / Hkv;
+
+  const int chunk = (Sk + num_splits - 1) / num_splits;
+  const int j0 = split * chunk;
+  const int j1 = min(Sk, j0 + chunk);
+
+  const uint16_t* kh = k + (size_t)bk * Sk * D;
+  const uint16_t* vh = v + (size_t)bk * Sk * D;
+
+  u32x4 qf[1][8];
+  const bool slot_used = n < G;
+  const size_t qrow = (size_t)b * Hq + (size_t)hkv * G + n;  // Sq == 1
+#pragma unroll
+  for (int st = 0; st < 8; ++st) {
+    if (slot_used)
+      qf[0][st] = *reinterpret_cast<const u32x4*>(q + qrow * D + 16 * st + 8 * g);
+    else
+      qf[0][st] = u32x4{0, 0, 0, 0};
+  }
+
+  f32x16 acc[4][1];
+  float m[1] = {-INFINITY}, l[1] = {0.0f};
+#pragma unroll
+  for (int db = 0; db < 4; ++db) acc[db][0] = f32x16{};
+
+  unsigned char ATTN_LDS* kt = (unsigned char ATTN_LDS*)(smem);
+  unsigned char ATTN_LDS* vt = kt + TILE_BYTES;
+  for (int key0 = j0; key0 < j1; key0 += KT) {
+#pragma unroll
+    for (int c = 0; c < KT / 4; ++c) load_rows_1k<false>(kh, key0, c, j1 - 1, kt);
+#pragma unroll
+    for (int c = 0; c < KT / 4; ++c) load_rows_1k<true>(vh, key0, c, j1 - 1, vt);
+    vm_wait_all();
+    tile_step<DT, 1>(kt, vt, qf, acc, m, l, scale_log2, key0 + KT > j1, key0, 0, j1, false, 0);
+    // every LDS read of this tile has been consumed by the MFMAs above before
+    // the next iteration's loads are issued (single wave, in-order issue)
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  }
+
+  const float lt = half_sum(l[0]);
+  const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+  if (slot_used) {
+    const size_t prow = qrow * num_splits + split;
+    float* op = o_part + prow * D;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int d0 = 32 * db + 8 * jj + 4 * g;
+        float4 w = make_float4(acc[db][0][4 * jj] * inv, acc[db][0][4 * jj + 1] * inv,
+                               acc[db][0][4 * jj + 2] * inv, acc[db][0][4 * jj + 3] * inv);
+        *reinterpret_cast<float4*>(op + d0) = w;
+      }
+    if (g == 0)
+      lse_part[prow] =
+          lt > 0.0f ? 0.69314718055994531f * (m[0] + __builtin_amdgcn_logf(lt)) : -INFINITY;
+  }
+}
+
+// One workgroup of D threads per (batch, query head); thread c owns column c.
+template <int DT>
+__global__ __launch_bounds__(D) void fa_combine_kernel(const float* __restrict__ o_part,
+                                                        const float* __restrict__ lse_part,
+                                                        uint16_t* __restrict__ o,
+                                                        float* __restrict__ lse, int num_splits) {
+  const int r = blockIdx.x;
+  const int c = threadIdx.x;
+  const float* ls = lse_part + (size_t)r * num_splits;
+  float M = -INFINITY;
+  for (int s = 0; s < num_splits; ++s) M = fmaxf(M, ls[s]);
+  float out = 0.0f, L = 0.0f;
+  if (M != -INFINITY) {
+    float accum = 0.0f;
+    for (int s = 0; s < num_splits; ++s) {
+      const float w = __expf(ls[s] - M);  // exp(-inf) = 0 for empty splits
+      L += w;
+      accum += w * o_part[((size_t)r * num_splits + s) * D + c];
+    }
+    out = accum / L;
+  }
+  if constexpr (DT == 0) {
+    _Float16 h = (_Float16)out;
+    o[(size_t)r * D + c] = __builtin_bit_cast(uint16_t, h);
+  } else {
+    __bf16 h = (__bf16)out;
+    o[(size_t)r * D + c] = __builtin_bit_cast(uint16_t, h);
+  }
+  if (lse != nullptr && c == 0) lse[r] = (M == -INFINITY) ? -INFINITY : M + __logf(L);
+}
+
+hipError_t launch_decode_split(const DecodeArgs& a, hipStream_t stream) {
+  const long long items = (long long)a.B * a.Hkv * a.num_splits;
+  dim3 grid((unsigned)items), block(64);
+  auto q = static_cast<const uint16_t*>(a.q);
+  auto k = static_cast<const uint16_t*>(a.k);
+  auto v = static_cast<const uint16_t*>(a.v);
+  if (a.dtype == 0)
+    hipLaunchKernelGGL((fa_decode_split_kernel<0>), grid, block, 0, stream, q, k, v, a.o_part,
+                       a.lse_part, a.Hq, a.Hkv, a.Sk, a.num_splits, a.scale_log2);
+  else
+    hipLaunchKernelGGL((fa_decode_split_kernel<1>), grid, block, 0, stream, q, k, v, a.o_part,
+                       a.lse_part, a.Hq, a.Hkv, a.Sk, a.num_splits, a.scale_log2);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
+  dim3 grid((unsigned)a.rows), block(D);
+  auto o = static_cast<uint16_t*>(a.o);
+  if (a.dtype == 0)
+    hipLaunchKernelGGL((fa_combine_kernel<0>), grid, block, 0, stream, a.o_part, a.lse_part, o,
+                       a.lse, a.num_splits);
+  else
+    hipLaunchKernelGGL((fa_combine_kernel<1>), grid, block, 0, stream, a.o_part, a.lse_part, o,
+                       a.lse, a.num_splits);
+  return hipGetLastError();
+}
+
+}  // namespace attn

@@ -1,0 +1,65 @@
+// Internal launchers shared between the kernel sources and the C ABI layer.
+// Arguments are already validated by the caller; each launcher only enqueues.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+constexpr int HEAD_DIM = 128;  // the head dimension the kernels implement
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int B, Hq, Hkv, Sq, Sk;
+  int causal;
+  float scale_log2;  // scale * log2(e), rounded once to fp32 on the host
+  int dtype;
+};
+
+struct DecodeArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  float* o_part;    // [B, Hq, num_splits, D] fp32
+  float* lse_part;  // [B, Hq, num_splits] fp32, natural log
+  int B, Hq, Hkv, Sk;
+  int num_splits;
+  float scale_log2;
+  int dtype;
+};
+
+struct CombineArgs {
+  const float* o_part;
+  const float* lse_part;
+  void* o;
+  float* lse;
+  int rows;  // B * Hq
+  int num_splits;
+  int dtype;
+};
+
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_decode_split(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
+
+// Number of 32-query blocks per wave and waves per workgroup of the prefill kernel.
+#ifndef ATTN_FWD_QB
+#define ATTN_FWD_QB 1
+#endif
+#ifndef ATTN_FWD_NW
+#define ATTN_FWD_NW 4
+#endif
+#ifndef ATTN_FWD_WPE
+#define ATTN_FWD_WPE 2
+#endif
+constexpr int FWD_QB = ATTN_FWD_QB;
+constexpr int FWD_NW = ATTN_FWD_NW;
+constexpr int FWD_WAVES_PER_SIMD = ATTN_FWD_WPE;  // occupancy the register budget is sized for
+constexpr int FWD_BR = FWD_QB * FWD_NW * 32;  // query rows per workgroup
+
+}  // namespace attn
