@@ -1,0 +1,239 @@
+"""Benchmark of the gfx950 attention forward path on one MI355X.
+
+One step is one pass of the whole hot path over one batch of synthetic input:
+
+  * prefill forward, bf16, causal, B=2, H=16, S=8192, d=128 (the headline
+    workload; FLOPs counted as 4*B*H*Sq*Sk*d, halved for causal), and
+  * split-KV decode, bf16, B=64, Hq=32, Hkv=8, Sk=8192, 16 splits, plus its
+    LSE combine (reported in HBM GB/s of algorithmic bytes).
+
+Inputs are seeded N(0,1) values already resident in HBM when the timed region
+starts.  Kernel durations come from HIP events recorded on the stream the
+library launches on (torch's current stream).  `value` is the prefill
+throughput in TFLOP/s; the decode rate, a GEMM ceiling measured on the same
+GPU, the roofline of the dominant kernel and the FP64 CPU oracle timed on a
+bounded sample of the prefill workload are reported beside it.  The oracle's
+sample also checks the GPU output on those rows; a failing check prints no
+throughput.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+import attention_forward_amd as A
+from attention_forward_amd.synthetic import BF16, WORKLOADS, bits, make_workload_inputs
+
+PREFILL = WORKLOADS["fwd_bf16_causal_b2_h16_s8192"]
+DECODE = WORKLOADS["decode_bf16_b64_hq32_hkv8_sk8192_split16"]
+METRIC = "attention fwd TFLOP/s and % of MFMA ceiling (S=8k d=128); decode HBM GB/s"
+PEAK_MFMA_TFLOPS = 2500.0   # MI355X dense fp16/bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+
+
+def decode_algorithmic_bytes(w) -> int:
+    """K and V read once per kv head, Q read, O (dtype) and LSE (fp32) written."""
+    e = 2
+    kv = 2 * w.B * w.Hkv * w.Sk * w.d * e
+    q = w.B * w.Hq * w.d * e
+    o = w.B * w.Hq * w.d * e
+    lse = w.B * w.Hq * 4
+    return kv + q + o + lse
+
+
+def gemm_ceiling(dtype, n=8192, iters=20):
+    a = torch.randn(n, n, device="cuda", dtype=dtype)
+    b = torch.randn(n, n, device="cuda", dtype=dtype)
+    for _ in range(3):
+        torch.matmul(a, b)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(iters):
+        torch.matmul(a, b)
+    e.record()
+    e.synchronize()
+    ms = s.elapsed_time(e) / iters
+    del a, b
+    return 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+
+
+def cpu_baseline(q, k, v, o_gpu, target_s: float):
+    """The oracle as it stands, timed on the host cores over a uniform random
+    sample of the prefill rows; also checks the GPU rows of that sample."""
+    import oracle
+
+    w = PREFILL
+    nthreads = len(os.sched_getaffinity(0))
+    qb, kb, vb = bits(q), bits(k), bits(v)
+    n_rows = w.B * w.Hq * w.Sq
+    flops_per_row = w.flops / n_rows  # the metric's counting convention, per row
+    rng = np.random.default_rng(0)
+    # calibrate on a small sample, then size the timed sample to ~target_s
+    probe = np.sort(rng.choice(n_rows, 256, replace=False)).astype(np.int64)
+    t0 = time.perf_counter()
+    oracle.attention_rows(qb, kb, vb, w.dtype, w.causal, w.scale, probe, want_ref=False,
+                          nthreads=nthreads)
+    dt = time.perf_counter() - t0
+    n = int(min(n_rows, max(512, 256 * target_s / max(dt, 1e-3))))
+    rows = np.sort(rng.choice(n_rows, n, replace=False)).astype(np.int64)
+    t0 = time.perf_counter()
+    o, lse, o_ref = oracle.attention_rows(qb, kb, vb, w.dtype, w.causal, w.scale, rows,
+                                          want_ref=True, nthreads=nthreads)
+    dt = time.perf_counter() - t0
+    og = o_gpu.reshape(-1, w.d)[torch.from_numpy(rows)].double().numpy()
+    err = float(np.abs(og - o).max())
+    bound = float(2 * np.abs(o_ref - o).max() + 1e-5)
+    base = {
+        "value": round(flops_per_row * n / dt / 1e12, 6), "unit": "TFLOP/s", "cores": nthreads,
+        "kind": "oracle",
+        "sample": "%d uniform random query rows of %s (FP64, %.1f s wall, %d threads)"
+                  % (n, w.name, dt, nthreads),
+    }
+    parity = {"rows": n, "max_abs": err, "bound": bound, "pass": err <= bound}
+    return base, parity
+
+
+def decode_parity(q, k, v, o_gpu, n_rows=64):
+    import oracle
+
+    w = DECODE
+    rng = np.random.default_rng(1)
+    rows = np.sort(rng.choice(w.B * w.Hq, n_rows, replace=False)).astype(np.int64)
+    o, _, o_ref = oracle.attention_rows(bits(q), bits(k), bits(v), w.dtype, False, w.scale, rows)
+    og = o_gpu.reshape(-1, w.d)[torch.from_numpy(rows)].double().numpy()
+    err = float(np.abs(og - o).max())
+    bound = float(2 * np.abs(o_ref - o).max() + 1e-5)
+    return {"rows": n_rows, "max_abs": err, "bound": bound, "pass": err <= bound}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target wall time of the oracle's CPU-baseline sample")
+    ap.add_argument("--skip-cpu-baseline", action="store_true",
+                    help="for profiler runs: no oracle leg (and no parity rows)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this library has no multi-GPU path "
+              "(requested --gpus %d)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    A.lib()  # fail loudly if libattn.so is not built
+    dev = torch.device("cuda", 0)
+
+    # inputs resident in HBM before the timed region
+    q, k, v = make_workload_inputs(PREFILL)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    o = torch.empty_like(qd)
+    lse = torch.empty(qd.shape[:3], device=dev, dtype=torch.float32)
+    dq, dk, dv = make_workload_inputs(DECODE)
+    dqd, dkd, dvd = dq.to(dev), dk.to(dev), dv.to(dev)
+    do = torch.empty_like(dqd)
+    dlse = torch.empty((DECODE.B, DECODE.Hq), device=dev, dtype=torch.float32)
+    ws = torch.empty(A.attn_decode_workspace_bytes(DECODE.B, DECODE.Hq, DECODE.d,
+                                                   DECODE.num_splits), device=dev,
+                     dtype=torch.uint8)
+
+    def step(ev=None):
+        if ev:
+            ev[0].record()
+        A.attn_fwd(qd, kd, vd, causal=True, scale=PREFILL.scale, out=o, lse=lse)
+        if ev:
+            ev[1].record()
+        A.attn_fwd_decode(dqd, dkd, dvd, DECODE.num_splits, scale=DECODE.scale, out=do, lse=dlse,
+                          workspace=ws)
+        if ev:
+            ev[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pre_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    dec_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    pre_avg = sum(pre_ms) / len(pre_ms)
+    dec_avg = sum(dec_ms) / len(dec_ms)
+    tflops = PREFILL.flops / (pre_avg * 1e-3) / 1e12
+    dec_bytes = decode_algorithmic_bytes(DECODE)
+    dec_gbs = dec_bytes / (dec_avg * 1e-3) / 1e9
+
+    gemm = {"bf16_8192^3": round(gemm_ceiling(torch.bfloat16), 1),
+            "fp16_8192^3": round(gemm_ceiling(torch.float16), 1)}
+    gemm_best = max(gemm.values())
+
+    result = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "attention fwd bf16 causal B=2 H=16 Sq=Sk=8192 d=128 + split-KV decode "
+                        "bf16 B=64 Hq=32 Hkv=8 Sk=8192 16 splits",
+            "prefill": {"B": PREFILL.B, "Hq": PREFILL.Hq, "Hkv": PREFILL.Hkv, "Sq": PREFILL.Sq,
+                        "Sk": PREFILL.Sk, "d": PREFILL.d, "causal": True},
+            "decode": {"B": DECODE.B, "Hq": DECODE.Hq, "Hkv": DECODE.Hkv, "Sk": DECODE.Sk,
+                       "d": DECODE.d, "num_splits": DECODE.num_splits},
+            "parallelism": "none (1 GPU)",
+        },
+        "prefill": {"ms": round(pre_avg, 4), "tflops": round(tflops, 2),
+                    "frac_mfma_peak": round(tflops / PEAK_MFMA_TFLOPS, 4),
+                    "frac_gemm_ceiling": round(tflops / gemm_best, 4),
+                    "flops": PREFILL.flops, "exp2_per_launch": PREFILL.flops // (4 * PREFILL.d)},
+        "decode": {"ms": round(dec_avg, 4), "value": round(dec_gbs, 1), "unit": "GB/s",
+                   "frac_hbm_peak": round(dec_gbs / PEAK_HBM_GBS, 4),
+                   "algorithmic_bytes": dec_bytes},
+        "gemm_ceiling_tflops": gemm,
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_MFMA_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_MFMA_TFLOPS, 4),
+                     "traffic": None, "kernel": "fa_fwd_kernel (bf16)"},
+        "roofline_decode": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": PEAK_HBM_GBS,
+                            "unit": "GB/s", "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
+                            "traffic": None,
+                            "kernel": "fa_decode_split_kernel + fa_combine_kernel (bf16)"},
+        "cpu_baseline": None,
+    }
+    ok = True
+    if not args.skip_cpu_baseline:
+        o_host = o.cpu()
+        base, parity = cpu_baseline(q, k, v, o_host, args.cpu_seconds)
+        result["cpu_baseline"] = base
+        result["parity"] = {"prefill": parity, "decode": decode_parity(dq, dk, dv, do.cpu())}
+        ok = parity["pass"] and result["parity"]["decode"]["pass"]
+    if not ok:
+        result["value"] = None
+        print(json.dumps(result))
+        sys.exit(1)
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()
