@@ -33,6 +33,9 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((__vector_size__(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 #define ATTN_LDS __attribute__((address_space(3)))
 
@@ -50,15 +53,11 @@ __device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
 // Round two floats to the 16-bit dtype (round to nearest even) and pack them.
 template <int DT>
 __device__ __forceinline__ unsigned pack2(float lo, float hi) {
-  if constexpr (DT == 0) {
-    _Float16 a = (_Float16)lo, b = (_Float16)hi;
-    return (unsigned)__builtin_bit_cast(unsigned short, a) |
-           ((unsigned)__builtin_bit_cast(unsigned short, b) << 16);
-  } else {
-    __bf16 a = (__bf16)lo, b = (__bf16)hi;
-    return (unsigned)__builtin_bit_cast(unsigned short, a) |
-           ((unsigned)__builtin_bit_cast(unsigned short, b) << 16);
-  }
+  const f32x2 v = {lo, hi};
+  if constexpr (DT == 0)
+    return __builtin_bit_cast(unsigned, __builtin_convertvector(v, f16x2));
+  else
+    return __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2));
 }
 
 // Value of x in lane l ^ 32 combined with x: returns (x_lo, x_hi) pair per lane.
@@ -123,50 +122,125 @@ __device__ __forceinline__ void load_rows_1k(const uint16_t* src_head, int key_b
 
 __device__ __forceinline__ void vm_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// ---- LDS operand reads with immediate offsets and data-dependent waits ----
+// The reads are issued through inline asm so that the compiler neither hoists
+// them nor inserts a wait on the direct-to-LDS loads of the next tile (which
+// write the other buffer); each consumer first executes an s_waitcnt that
+// takes the loaded registers as operands, so it cannot be scheduled before it.
+template <int OFF>
+__device__ __forceinline__ u32x4 lds_b128(unsigned addr) {
+  u32x4 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
+  return r;
+}
+template <int OFF>
+__device__ __forceinline__ u32x2 lds_tr16(unsigned addr) {
+  u32x2 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
+  return r;
+}
+template <int N>
+__device__ __forceinline__ void lgkm_wait(u32x4& x) {
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(x) : "n"(N));
+}
+
+// Per-lane LDS byte addresses (relative to a K/V stage) that stay fixed for
+// the whole key loop; tile, stage and step offsets are immediates.
+struct LaneAddr {
+  unsigned k[8];  // K operand of d-step st (key block 0; block 1 is +32 rows)
+  unsigned v[4];  // V^T operand of d-block db (key step 0; others are row offsets)
+};
+
+__device__ __forceinline__ LaneAddr lane_addresses() {
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 5, n = lane & 31, j = lane & 15, h = (lane >> 4) & 1;
+  LaneAddr a;
+#pragma unroll
+  for (int st = 0; st < 8; ++st)
+    a.k[st] = (unsigned)(n * ROW + (((2 * st + g) ^ k_swz(n)) * 16));
+  // V^T reads: rows 4g + (j>>2) (+16t, +32kb, +8 for items 4..7), 32-byte column
+  // group 4db + 2h, 8-byte half (j&3)>>1 ... see v_swz
+  const int row_l = 4 * g + (j >> 2);
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+    const int slot = 4 * db + 2 * h + ((j & 3) >> 1);
+    a.v[db] = (unsigned)(row_l * ROW + ((slot ^ v_swz(row_l)) * 16) + 8 * (j & 1));
+  }
+  return a;
+}
+
 // ---- one 64-key tile for QB blocks of 32 queries owned by this wave ----
 //
-// kt, vt: LDS tiles (swizzled).  qf: Q^T operands [QB][8] (16-deep d steps).
-// o: O^T accumulators [4 d-blocks][QB].  m: running max (log2 units, -inf
-// initially); l: this lane's partial running sum (the lane's half of the keys).
-// key0: global index of the tile's first key; qrow0: global index of this
-// wave's first query; mask: apply the key-validity / causal test per score.
-// Online softmax across tiles: "The FA5090 Optimization Journey", sec. 2.6
-// (exp2 with log2 e folded into the scale, running max in the log2 domain,
-// sec. 2.8 for the effective max of a fully masked tile); "10 rounds of
-// hand-written fused attention ...", round R8 (m and l carried across tiles).
-template <int DT, int QB>
-__device__ __forceinline__ void tile_step(const unsigned char ATTN_LDS* kt,
-                                          const unsigned char ATTN_LDS* vt, const u32x4 (&qf)[QB][8],
-                                          f32x16 (&o)[4][QB], float (&m)[QB], float (&l)[QB],
-                                          float scale_log2, bool mask, int key0, int qrow0,
-                                          int n_keys, bool causal, int causal_off) {
+// base: LDS address of the stage (K at +0, V at +TILE_BYTES).  qf: Q^T operands
+// [QB][8] (16-deep d steps).  o: O^T accumulators [4 d-blocks][QB].  m: running
+// max (log2 units, -inf initially); l: this lane's partial running sum (the
+// lane's half of the keys).  key0: global index of the tile's first key;
+// qrow0: global index of this wave's first query.  MASK: apply the key-validity
+// and causal test per score (only tiles that cross the diagonal or the end of
+// the keys; "The FA5090 Optimization Journey", sec. 2.8, mask specialisation).
+// Online softmax across tiles: sec. 2.6 (exp2 with log2 e folded into the
+// scale, running max in the log2 domain), sec. 2.8 (effective max of a fully
+// masked tile); "10 rounds of hand-written fused attention ...", round R8.
+template <int DT, int QB, bool MASK>
+__device__ __forceinline__ void tile_step(unsigned base, const LaneAddr& la,
+                                          const u32x4 (&qf)[QB][8], f32x16 (&o)[4][QB],
+                                          float (&m)[QB], float (&l)[QB], float scale_log2,
+                                          int key0, int qrow0, int n_keys, bool causal,
+                                          int causal_off) {
   const int lane = threadIdx.x & 63;
   const int g = lane >> 5;
   const int n = lane & 31;
 
-  // S^T = K Q^T : two 32-key blocks x QB query blocks, 8 steps of 16 d.
+  // ---- S^T = K Q^T: 2 key blocks x 8 d-steps, K operands 8 reads ahead ----
   f32x16 s[2][QB];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
+  for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) s[kb][qb] = f32x16{};
-    const int row = 32 * kb + n;
-#pragma unroll
-    for (int st = 0; st < 8; ++st) {
-      const int slot = (2 * st + g) ^ k_swz(row);
-      u32x4 a = *reinterpret_cast<const ATTN_LDS u32x4*>(kt + row * ROW + slot * 16);
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) s[kb][qb] = mfma<DT>(a, qf[qb][st], s[kb][qb]);
+  u32x4 ko[8];
+  auto read_k = [&](int i, u32x4& dst) {
+    // i = kb * 8 + st
+#define ATTN_KREAD(I)                                                                  \
+  case I:                                                                              \
+    dst = lds_b128<((I) >> 3) * 32 * ROW>(base + la.k[(I) & 7]);           \
+    break;
+    switch (i) {
+      ATTN_KREAD(0) ATTN_KREAD(1) ATTN_KREAD(2) ATTN_KREAD(3) ATTN_KREAD(4) ATTN_KREAD(5)
+      ATTN_KREAD(6) ATTN_KREAD(7) ATTN_KREAD(8) ATTN_KREAD(9) ATTN_KREAD(10) ATTN_KREAD(11)
+      ATTN_KREAD(12) ATTN_KREAD(13) ATTN_KREAD(14) ATTN_KREAD(15)
     }
+#undef ATTN_KREAD
+  };
+#pragma unroll
+  for (int i = 0; i < 8; ++i) read_k(i, ko[i]);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    u32x4& cur = ko[i & 7];
+    // reads issued so far: min(16, 8 + i); read i is done when at most
+    // (issued - i - 1) younger ones are outstanding
+    switch ((i + 8 < 16 ? 7 : 15 - i)) {
+      case 7: lgkm_wait<7>(cur); break;
+      case 6: lgkm_wait<6>(cur); break;
+      case 5: lgkm_wait<5>(cur); break;
+      case 4: lgkm_wait<4>(cur); break;
+      case 3: lgkm_wait<3>(cur); break;
+      case 2: lgkm_wait<2>(cur); break;
+      case 1: lgkm_wait<1>(cur); break;
+      default: lgkm_wait<0>(cur); break;
+    }
+    const int kb = i >> 3, st = i & 7;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) s[kb][qb] = mfma<DT>(cur, qf[qb][st], s[kb][qb]);
+    if (i + 8 < 16) read_k(i + 8, ko[i & 7]);
   }
 
-  // visibility of the score in register r of key block kb for query block qb
+  // ---- mask (tiles crossing the diagonal / the end of the keys only) ----
   auto hidden = [&](int kb, int qb, int r) {
     const int key = key0 + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
     const int qi = qrow0 + 32 * qb + n;
     return key >= n_keys || (causal && key > qi + causal_off);
   };
-  if (mask) {
+  if constexpr (MASK) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -176,18 +250,19 @@ __device__ __forceinline__ void tile_step(const unsigned char ATTN_LDS* kt,
           if (hidden(kb, qb, r)) s[kb][qb][r] = -INFINITY;
   }
 
-  // online softmax, per query block
+  // ---- online softmax, per query block ----
   u32x4 pf[2][2][QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    float mx = s[0][qb][0];
+    float mx = fmaxf(s[0][qb][0], s[0][qb][1]);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][qb][r]);
+      for (int r = (kb == 0 ? 2 : 0); r < 16; ++r) mx = fmaxf(mx, s[kb][qb][r]);
     mx = half_max(mx);
     // -inf * 0 would be NaN when scale is 0; a fully hidden tile keeps m
-    const float mxs = (mx == -INFINITY) ? -INFINITY : mx * scale_log2;
+    float mxs = mx * scale_log2;
+    if constexpr (MASK) mxs = (mx == -INFINITY) ? -INFINITY : mxs;
     const float m_new = fmaxf(m[qb], mxs);
     const float m_eff = (m_new == -INFINITY) ? 0.0f : m_new;
     const float alpha = __builtin_amdgcn_exp2f(m[qb] - m_eff);
@@ -198,67 +273,65 @@ __device__ __forceinline__ void tile_step(const unsigned char ATTN_LDS* kt,
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][qb][r], scale_log2, -m_eff));
-        if (mask && hidden(kb, qb, r)) p = 0.0f;  // exact zero even when scale is 0
+        if constexpr (MASK) p = hidden(kb, qb, r) ? 0.0f : p;  // exact zero even for scale 0
         s[kb][qb][r] = p;
         rs += p;
       }
     l[qb] = l[qb] * alpha + rs;
-    // alpha == 1 (the max did not move) leaves O bit-identical: skip the
-    // multiply when that holds for the whole wave ("The FA5090 Optimization
-    // Journey", sec. 2.8, identity rescale-skip decided by a wave-wide vote).
-    if (__ballot(alpha != 1.0f)) {
+    // Unconditional: a wave-uniform skip when alpha == 1 ("The FA5090
+    // Optimization Journey", sec. 2.8) makes the compiler copy the whole
+    // accumulator at the branch merge, which costs more than the 64 multiplies.
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[db][qb][r] *= alpha;
-    }
+    for (int db = 0; db < 4; ++db) o[db][qb] *= alpha;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         u32x4 w;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = pack2<DT>(s[kb][qb][8 * t + 2 * e], s[kb][qb][8 * t + 2 * e + 1]);
+        for (int e = 0; e < 4; ++e)
+          w[e] = pack2<DT>(s[kb][qb][8 * t + 2 * e], s[kb][qb][8 * t + 2 * e + 1]);
         pf[kb][t][qb] = w;
       }
   }
 
-  // O^T += V^T P^T : 4 blocks of 32 d x 4 steps of 16 keys.  Operands for step
-  // i+1 are read while the MFMA of step i runs.
-  const int j = lane & 15;
-  const int h = (lane >> 4) & 1;
-  // rows 32kb + 16t + 4g + (j>>2) (+8 for the second half); their swizzle only
-  // depends on j>>2, so only the d-block changes the slot XOR
-  const int row_l = 4 * g + (j >> 2);
-  const int sw = v_swz(row_l);
-  const unsigned lane_base = (unsigned)(row_l * ROW + 8 * (j & 1));
-  auto v_operand_addr = [&](int db) {
-    const int slot = 4 * db + 2 * h + ((j & 3) >> 1);
-    return lane_base + (unsigned)((slot ^ sw) * 16);
-  };
-  const unsigned vbase = (unsigned)(size_t)vt;
-  u32x4 va[2];
-  auto read_v = [&](int step, u32x4& dst) {
-    const int db = step >> 2, kb = (step >> 1) & 1, t = step & 1;
-    const unsigned addr = vbase + v_operand_addr(db) + (unsigned)((32 * kb + 16 * t) * ROW);
+  // ---- O^T += V^T P^T: 4 d-blocks x 4 key steps, operands 4 steps ahead ----
+  // step i: db = i >> 2, kb = (i >> 1) & 1, t = i & 1; the operand's two
+  // transposing reads cover keys 32kb + 16t + 4g + {0..3} and the same + 8.
+  u32x4 vo[4];
+  auto read_v = [&](int i, u32x4& dst) {
     u32x2 lo, hi;
-    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(lo) : "v"(addr));
-    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:2048" : "=v"(hi) : "v"(addr));
+#define ATTN_VREAD(I)                                                                       \
+  case I:                                                                                   \
+    lo = lds_tr16<TILE_BYTES + (32 * (((I) >> 1) & 1) + 16 * ((I) & 1)) * ROW>(   \
+        base + la.v[(I) >> 2]);                                                             \
+    hi = lds_tr16<TILE_BYTES + (32 * (((I) >> 1) & 1) + 16 * ((I) & 1) + 8) *     \
+                                               ROW>(base + la.v[(I) >> 2]);                 \
+    break;
+    switch (i) {
+      ATTN_VREAD(0) ATTN_VREAD(1) ATTN_VREAD(2) ATTN_VREAD(3) ATTN_VREAD(4) ATTN_VREAD(5)
+      ATTN_VREAD(6) ATTN_VREAD(7) ATTN_VREAD(8) ATTN_VREAD(9) ATTN_VREAD(10) ATTN_VREAD(11)
+      ATTN_VREAD(12) ATTN_VREAD(13) ATTN_VREAD(14) ATTN_VREAD(15)
+    }
+#undef ATTN_VREAD
     dst = u32x4{lo[0], lo[1], hi[0], hi[1]};
   };
-  read_v(0, va[0]);
 #pragma unroll
-  for (int step = 0; step < 16; ++step) {
-    u32x4& cur = va[step & 1];
-    if (step + 1 < 16) {
-      read_v(step + 1, va[(step + 1) & 1]);
-      asm volatile("s_waitcnt lgkmcnt(2)" : "+v"(cur));
-    } else {
-      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(cur));
+  for (int i = 0; i < 4; ++i) read_v(i, vo[i]);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    u32x4& cur = vo[i & 3];
+    // two reads per operand; operands issued so far: min(16, 4 + i)
+    switch (i + 4 < 16 ? 6 : 2 * (15 - i)) {
+      case 6: lgkm_wait<6>(cur); break;
+      case 4: lgkm_wait<4>(cur); break;
+      case 2: lgkm_wait<2>(cur); break;
+      default: lgkm_wait<0>(cur); break;
     }
-    const int db = step >> 2, kb = (step >> 1) & 1, t = step & 1;
+    const int db = i >> 2, kb = (i >> 1) & 1, t = i & 1;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) o[db][qb] = mfma<DT>(cur, pf[kb][t][qb], o[db][qb]);
+    if (i + 4 < 16) read_v(i + 4, vo[i & 3]);
   }
 }
 

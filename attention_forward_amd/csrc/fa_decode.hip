@@ -60,15 +60,20 @@ __global__ __launch_bounds__(64, 2) void fa_decode_split_kernel(
 
   unsigned char ATTN_LDS* kt = (unsigned char ATTN_LDS*)(smem);
   unsigned char ATTN_LDS* vt = kt + TILE_BYTES;
+  const LaneAddr la = lane_addresses();
+  const unsigned base = (unsigned)(size_t)kt;
   for (int key0 = j0; key0 < j1; key0 += KT) {
 #pragma unroll
     for (int c = 0; c < KT / 4; ++c) load_rows_1k<false>(kh, key0, c, j1 - 1, kt);
 #pragma unroll
     for (int c = 0; c < KT / 4; ++c) load_rows_1k<true>(vh, key0, c, j1 - 1, vt);
     vm_wait_all();
-    tile_step<DT, 1>(kt, vt, qf, acc, m, l, scale_log2, key0 + KT > j1, key0, 0, j1, false, 0);
-    // every LDS read of this tile has been consumed by the MFMAs above before
-    // the next iteration's loads are issued (single wave, in-order issue)
+    if (key0 + KT > j1)
+      tile_step<DT, 1, true>(base, la, qf, acc, m, l, scale_log2, key0, 0, j1, false, 0);
+    else
+      tile_step<DT, 1, false>(base, la, qf, acc, m, l, scale_log2, key0, 0, j1, false, 0);
+    // every LDS read of this tile has completed (the MFMAs consumed them)
+    // before the next iteration's loads overwrite the stage
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   }
 

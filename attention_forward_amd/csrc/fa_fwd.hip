@@ -97,6 +97,8 @@ __global__ __launch_bounds__(NW * 64, FWD_WAVES_PER_SIMD) void fa_fwd_kernel(con
 
   const int wave_last_q = min(qw0 + QB * 32, Sq) - 1;
   const bool wave_active = qw0 < Sq;
+  const LaneAddr la = lane_addresses();
+  const unsigned smem_base = (unsigned)(size_t)(unsigned char ATTN_LDS*)(smem);
 
   if (n_tiles > 0) issue_tile(0);
   for (int j = 0; j < n_tiles; ++j) {
@@ -108,10 +110,12 @@ __global__ __launch_bounds__(NW * 64, FWD_WAVES_PER_SIMD) void fa_fwd_kernel(con
     if (wave_active && !hidden) {
       const bool need_mask =
           (key0 + KT > Sk) || (causal && key0 + KT - 1 > qw0 + causal_off);
-      const unsigned char ATTN_LDS* base =
-          (const unsigned char ATTN_LDS*)(smem) + (j & 1) * 2 * TILE_BYTES;
-      tile_step<DT, QB>(base, base + TILE_BYTES, qf, acc, m, l, scale_log2, need_mask, key0, qw0,
-                        Sk, causal != 0, causal_off);
+      const unsigned base = smem_base + (unsigned)((j & 1) * 2 * TILE_BYTES);
+      if (need_mask)
+        tile_step<DT, QB, true>(base, la, qf, acc, m, l, scale_log2, key0, qw0, Sk, causal != 0,
+                                causal_off);
+      else
+        tile_step<DT, QB, false>(base, la, qf, acc, m, l, scale_log2, key0, qw0, Sk, false, 0);
     }
   }
 

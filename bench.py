@@ -125,6 +125,11 @@ def main():
                     help="target wall time of the oracle's CPU-baseline sample")
     ap.add_argument("--skip-cpu-baseline", action="store_true",
                     help="for profiler runs: no oracle leg (and no parity rows)")
+    ap.add_argument("--skip-gemm", action="store_true",
+                    help="for profiler runs: do not measure the GEMM ceiling")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="after the timed region, run one plain device copy of this many MiB "
+                         "(a known-size kernel for scaling HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this library has no multi-GPU path "
@@ -178,9 +183,20 @@ def main():
     dec_bytes = decode_algorithmic_bytes(DECODE)
     dec_gbs = dec_bytes / (dec_avg * 1e-3) / 1e9
 
-    gemm = {"bf16_8192^3": round(gemm_ceiling(torch.bfloat16), 1),
-            "fp16_8192^3": round(gemm_ceiling(torch.float16), 1)}
-    gemm_best = max(gemm.values())
+    if args.copy_mib > 0:
+        src = torch.ones(args.copy_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    if args.skip_gemm:
+        gemm = {}
+        gemm_best = float("nan")
+    else:
+        gemm = {"bf16_8192^3": round(gemm_ceiling(torch.bfloat16), 1),
+                "fp16_8192^3": round(gemm_ceiling(torch.float16), 1)}
+        gemm_best = max(gemm.values())
 
     result = {
         "metric": METRIC,
