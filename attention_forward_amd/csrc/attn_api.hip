@@ -43,6 +43,9 @@ int hip_status(hipError_t e, const char* what) {
 float fold_log2e(float scale) { return (float)((double)scale * 1.4426950408889634074); }
 
 constexpr size_t kAlign = 256;
+// rows of one head are addressed through a buffer descriptor whose byte range
+// is 32-bit: S * 256 bytes must stay below 2^32
+constexpr int kMaxSeq = (1 << 24) - 1;
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 }  // namespace
@@ -74,6 +77,8 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
   const long long kv_elems = (long long)B * Hkv * Sk * d;
   if (items > INT_MAX || q_elems > (1LL << 46) || kv_elems > (1LL << 46))
     return fail(ATTN_ERR_SHAPE, "attn_fwd: problem too large for one launch");
+  if (Sq > kMaxSeq || Sk > kMaxSeq)
+    return fail(ATTN_ERR_SHAPE, "attn_fwd: sequence length above %d", kMaxSeq);
   int st = check_device();
   if (st != ATTN_OK) return st;
   attn::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, causal, fold_log2e(scale), dtype};
@@ -140,6 +145,7 @@ int attn_fwd_decode(const void* q, const void* k, const void* v, void* o, float*
   if ((long long)B * Hkv * num_splits > INT_MAX || (long long)B * Hq > INT_MAX ||
       (long long)B * Hkv * Sk * d > (1LL << 46))
     return fail(ATTN_ERR_SHAPE, "attn_fwd_decode: problem too large for one launch");
+  if (Sk > kMaxSeq) return fail(ATTN_ERR_SHAPE, "attn_fwd_decode: Sk above %d", kMaxSeq);
   int st = check_device();
   if (st != ATTN_OK) return st;
   const size_t rows = (size_t)B * Hq * num_splits;

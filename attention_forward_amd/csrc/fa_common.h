@@ -99,25 +99,42 @@ __device__ __forceinline__ int v_swz(int row) {
 }
 
 // ---- HBM -> LDS tile load ----
-// One wave instruction of global_load_lds moves 64 x 16 B into 1 KiB of LDS at
-// base + 16*lane, i.e. 4 full rows.  The lane that fills LDS slot p of row r
-// reads global slot p ^ swz(r) of that row, so LDS slot s ^ swz(r) holds the
-// row's logical slot s.  Rows past the last valid key are clamped to it (their
-// scores are masked, their values stay finite).
+// One wave instruction of a direct-to-LDS load moves 64 x 16 B into 1 KiB of
+// LDS at base + 16*lane, i.e. 4 full rows.  The lane that fills LDS slot p of
+// row r reads global slot p ^ swz(r) of that row, so LDS slot s ^ swz(r) holds
+// the row's logical slot s.
+// Per-lane byte offset, within a 1 KiB load chunk, of the 16-byte source slot
+// the lane fetches: row (chunk*4 + lane/16), slot (lane%16) ^ swz(row).  With
+// chunks stepping by 4 rows per wave and 16 rows per round, the row bits the
+// swizzles use are fixed per lane, so one offset serves a whole tile.
 template <bool IS_V>
-__device__ __forceinline__ void load_rows_1k(const uint16_t* src_head, int key_base, int chunk,
-                                             int last_key, unsigned char ATTN_LDS* tile) {
+__device__ __forceinline__ unsigned load_lane_offset(int chunk) {
   const int lane = threadIdx.x & 63;
   const int r = chunk * 4 + (lane >> 4);
-  const int p = lane & 15;
-  int key = key_base + r;
-  key = key > last_key ? last_key : key;
-  const int slot = p ^ (IS_V ? v_swz(r) : k_swz(r));
-  const unsigned char* g =
-      reinterpret_cast<const unsigned char*>(src_head) + (size_t)key * ROW + slot * 16;
-  __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(g),
-                                   reinterpret_cast<ATTN_LDS void*>(tile + chunk * 1024), 16, 0,
-                                   0);
+  const int slot = (lane & 15) ^ (IS_V ? v_swz(r) : k_swz(r));
+  return (unsigned)(r * ROW + slot * 16);
+}
+
+// ---- bounds-checked buffer loads ----
+// A raw buffer descriptor covers [base, base + bytes); a lane whose byte offset
+// falls outside reads zeros (into registers, or into LDS for the direct-to-LDS
+// form), so ragged tails need neither clamping nor branches.  bytes < 2^32.
+constexpr unsigned RSRC_WORD3 = 0x00020000u;  // gfx9 raw buffer, 32-bit data format
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, long long bytes) {
+  const int n = bytes <= 0 ? 0 : (int)(unsigned)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, RSRC_WORD3);
+}
+
+// 64 lanes x 16 bytes from rsrc at byte offsets voff -> LDS dst + 16 * lane
+__device__ __forceinline__ void load_chunk(__amdgpu_buffer_rsrc_t r, unsigned voff,
+                                           unsigned char ATTN_LDS* dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, reinterpret_cast<ATTN_LDS void*>(dst), 16, (int)voff,
+                                           0, 0, 0);
+}
+
+__device__ __forceinline__ u32x4 load_b128(__amdgpu_buffer_rsrc_t r, unsigned voff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0));
 }
 
 __device__ __forceinline__ void vm_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }

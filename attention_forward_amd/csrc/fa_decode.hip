@@ -42,15 +42,16 @@ __global__ __launch_bounds__(64, 2) void fa_decode_split_kernel(
   const uint16_t* kh = k + (size_t)bk * Sk * D;
   const uint16_t* vh = v + (size_t)bk * Sk * D;
 
+  // the group's query heads fill slots 0..G-1; slots past G read as zeros
   u32x4 qf[1][8];
   const bool slot_used = n < G;
   const size_t qrow = (size_t)b * Hq + (size_t)hkv * G + n;  // Sq == 1
+  {
+    const __amdgpu_buffer_rsrc_t qr =
+        make_rsrc(q + ((size_t)b * Hq + (size_t)hkv * G) * D, (long long)G * ROW);
+    const unsigned row_off = (unsigned)(n * ROW + 16 * g);
 #pragma unroll
-  for (int st = 0; st < 8; ++st) {
-    if (slot_used)
-      qf[0][st] = *reinterpret_cast<const u32x4*>(q + qrow * D + 16 * st + 8 * g);
-    else
-      qf[0][st] = u32x4{0, 0, 0, 0};
+    for (int st = 0; st < 8; ++st) qf[0][st] = load_b128(qr, row_off + 32 * st);
   }
 
   f32x16 acc[4][1];
@@ -62,11 +63,20 @@ __global__ __launch_bounds__(64, 2) void fa_decode_split_kernel(
   unsigned char ATTN_LDS* vt = kt + TILE_BYTES;
   const LaneAddr la = lane_addresses();
   const unsigned base = (unsigned)(size_t)kt;
+  // chunk c covers rows 4c + lane/16: the K swizzle repeats every 4 chunks,
+  // the V swizzle is the same for every chunk
+  unsigned koff[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) koff[c] = load_lane_offset<false>(c);
+  const unsigned voff = load_lane_offset<true>(0);
   for (int key0 = j0; key0 < j1; key0 += KT) {
+    const long long bytes = (long long)(j1 - key0) * ROW;  // keys past the split read as zeros
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kh + (size_t)key0 * D, bytes);
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(vh + (size_t)key0 * D, bytes);
 #pragma unroll
-    for (int c = 0; c < KT / 4; ++c) load_rows_1k<false>(kh, key0, c, j1 - 1, kt);
+    for (int c = 0; c < KT / 4; ++c) load_chunk(kr, koff[c & 3] + (c >> 2) * 16 * ROW, kt + c * 1024);
 #pragma unroll
-    for (int c = 0; c < KT / 4; ++c) load_rows_1k<true>(vh, key0, c, j1 - 1, vt);
+    for (int c = 0; c < KT / 4; ++c) load_chunk(vr, voff + c * 4 * ROW, vt + c * 1024);
     vm_wait_all();
     if (key0 + KT > j1)
       tile_step<DT, 1, true>(base, la, qf, acc, m, l, scale_log2, key0, 0, j1, false, 0);

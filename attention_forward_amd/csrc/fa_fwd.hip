@@ -59,20 +59,18 @@ __global__ __launch_bounds__(NW * 64, FWD_WAVES_PER_SIMD) void fa_fwd_kernel(con
   }
   const int n_tiles = (kv_end + KT - 1) / KT;
 
-  // Q^T operands: lane holds Q[row][16*st + 8*g .. +7] for its query n
+  // Q^T operands: lane holds Q[row][16*st + 8*g .. +7] for its query n; rows
+  // past Sq read as zeros
   u32x4 qf[QB][8];
+  {
+    const __amdgpu_buffer_rsrc_t qr = make_rsrc(qh, (long long)Sq * ROW);
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int row = qw0 + 32 * qb + n;
+    for (int qb = 0; qb < QB; ++qb) {
+      const unsigned row_off = (unsigned)((qw0 + 32 * qb + n) * ROW + 16 * g);
 #pragma unroll
-    for (int st = 0; st < 8; ++st) {
-      if (row < Sq)
-        qf[qb][st] = *reinterpret_cast<const u32x4*>(qh + (size_t)row * D + 16 * st + 8 * g);
-      else
-        qf[qb][st] = u32x4{0, 0, 0, 0};
+      for (int st = 0; st < 8; ++st) qf[qb][st] = load_b128(qr, row_off + 32 * st);
     }
   }
-
   f32x16 acc[4][QB];
   float m[QB], l[QB];
 #pragma unroll
@@ -83,16 +81,23 @@ __global__ __launch_bounds__(NW * 64, FWD_WAVES_PER_SIMD) void fa_fwd_kernel(con
     for (int db = 0; db < 4; ++db) acc[db][qb] = f32x16{};
   }
 
+  // lane offsets of this wave's load chunks: chunk c*NW + wave covers rows
+  // 16c + 4*wave + lane/16, so the swizzle pattern is the same for every c
+  static_assert(NW == 4, "one lane offset per wave needs chunks 16 rows apart");
+  const unsigned koff = load_lane_offset<false>(wave);
+  const unsigned voff = load_lane_offset<true>(wave);
   auto issue_tile = [&](int j) {
-    unsigned char ATTN_LDS* base = (unsigned char ATTN_LDS*)(smem) +
-                                   (j & 1) * 2 * TILE_BYTES;
+    unsigned char ATTN_LDS* base = (unsigned char ATTN_LDS*)(smem) + (j & 1) * 2 * TILE_BYTES;
     const int key0 = j * KT;
+    const long long bytes = (long long)(Sk - key0) * ROW;  // keys past Sk read as zeros
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kh + (size_t)key0 * D, bytes);
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(vh + (size_t)key0 * D, bytes);
 #pragma unroll
     for (int c = 0; c < CHUNKS_PER_WAVE; ++c)
-      load_rows_1k<false>(kh, key0, c * NW + wave, Sk - 1, base);
+      load_chunk(kr, koff + c * 16 * ROW, base + (c * NW + wave) * 1024);
 #pragma unroll
     for (int c = 0; c < CHUNKS_PER_WAVE; ++c)
-      load_rows_1k<true>(vh, key0, c * NW + wave, Sk - 1, base + TILE_BYTES);
+      load_chunk(vr, voff + c * 16 * ROW, base + TILE_BYTES + (c * NW + wave) * 1024);
   };
 
   const int wave_last_q = min(qw0 + QB * 32, Sq) - 1;

@@ -45,7 +45,7 @@ typedef enum { ATTN_F16 = 0, ATTN_BF16 = 1 } attn_dtype;
 typedef enum {
   ATTN_OK = 0,
   ATTN_ERR_NULL = 1,        /* a required pointer is NULL */
-  ATTN_ERR_SHAPE = 2,       /* non-positive size, Hq % Hkv != 0, size overflow */
+  ATTN_ERR_SHAPE = 2,       /* non-positive size, Hq % Hkv != 0, Sq or Sk >= 2^24, size overflow */
   ATTN_ERR_UNSUPPORTED = 3, /* valid but not implemented: d != 128, dtype, GQA group > 32 */
   ATTN_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
   ATTN_ERR_WORKSPACE = 5,   /* decode workspace missing or too small */

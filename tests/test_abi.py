@@ -70,6 +70,7 @@ def fwd(L, **kw):
     (dict(q=ctypes.c_void_p((1 << 20) + 8)), A.ATTN_ERR_ALIGN),
     (dict(lse=ctypes.c_void_p((1 << 20) + 2)), A.ATTN_ERR_ALIGN),
     (dict(B=1 << 20, Hq=1 << 10, Hkv=1 << 10, Sq=1 << 20), A.ATTN_ERR_SHAPE),
+    (dict(Sk=1 << 24), A.ATTN_ERR_SHAPE), (dict(Sq=1 << 24), A.ATTN_ERR_SHAPE),
     (dict(), A.ATTN_ERR_NO_DEVICE),
 ])
 def test_fwd_validation(L, kw, status):
@@ -92,7 +93,8 @@ def dec(L, **kw):
     (dict(ns=0), A.ATTN_ERR_VALUE), (dict(ns=101), A.ATTN_ERR_VALUE),
     (dict(wsb=16), A.ATTN_ERR_WORKSPACE), (dict(ws=None), A.ATTN_ERR_WORKSPACE),
     (dict(ws=ctypes.c_void_p((1 << 20) + 4)), A.ATTN_ERR_ALIGN), (dict(d=256), A.ATTN_ERR_UNSUPPORTED),
-    (dict(scale=-0.5), A.ATTN_ERR_VALUE), (dict(), A.ATTN_ERR_NO_DEVICE),
+    (dict(scale=-0.5), A.ATTN_ERR_VALUE), (dict(Sk=1 << 24, ns=4), A.ATTN_ERR_SHAPE),
+    (dict(), A.ATTN_ERR_NO_DEVICE),
 ])
 def test_decode_validation(L, kw, status):
     assert dec(L, **kw) == status
