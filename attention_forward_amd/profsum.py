@@ -1,0 +1,132 @@
+"""Summarise rocprofv3 CSV output into the short text summaries kept under profiles/.
+
+    # kernel durations (rocprofv3 --kernel-trace --stats -f csv ... -o NAME)
+    python -m attention_forward_amd.profsum stats DIR NAME --cmd "<command>" > profiles/X.md
+
+    # HBM bytes per dispatch from two --pmc runs (FETCH_SIZE, WRITE_SIZE), each scaled by
+    # what the same counter reads for a plain copy of --copy-mib MiB run in the same process
+    python -m attention_forward_amd.profsum traffic DIR FETCH_NAME WRITE_NAME --copy-mib 1024 \
+        --cmd-fetch "<command>" --cmd-write "<command>" --out profiles/traffic.json > profiles/Y.md
+
+Only parses files; it runs nothing on the GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+
+
+def kernel_sources_hash() -> str:
+    """sha256 over the HIP sources and headers the kernels are built from."""
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(HERE, "csrc", "*.h")) +
+                   glob.glob(os.path.join(HERE, "csrc", "*.hip")))
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
+def short(name: str) -> str:
+    name = name.replace("void ", "")
+    i = name.find("(")
+    return name if i < 0 else name[:i]
+
+
+def stats(d, name, cmd):
+    path = os.path.join(d, name + "_kernel_stats.csv")
+    rows = list(csv.DictReader(open(path)))
+    out = ["# Kernel durations", "", "Command:", "", "```", cmd, "```", "",
+           "| kernel | calls | average µs | min µs | max µs | share |",
+           "|---|---|---|---|---|---|"]
+    for r in rows:
+        out.append("| `%s` | %s | %.1f | %.1f | %.1f | %.1f%% |" % (
+            short(r["Name"]), r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+            float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+    return "\n".join(out) + "\n"
+
+
+def _counters(path):
+    agg = collections.defaultdict(lambda: collections.defaultdict(list))
+    for r in csv.DictReader(open(path)):
+        agg[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    return agg
+
+
+def traffic(d, fetch_name, write_name, copy_mib, cmd_fetch, cmd_write, out_json):
+    f = _counters(os.path.join(d, fetch_name + "_counter_collection.csv"))
+    w = _counters(os.path.join(d, write_name + "_counter_collection.csv"))
+    copy_kib = copy_mib * 1024.0
+
+    def find_copy(agg, counter):
+        for k, v in agg.items():
+            if COPY_KERNEL in k and counter in v:
+                return max(v[counter])
+        raise SystemExit("no %s dispatch with %s in the counter file" % (COPY_KERNEL, counter))
+
+    f_scale = copy_kib / find_copy(f, "FETCH_SIZE")
+    w_scale = copy_kib / find_copy(w, "WRITE_SIZE")
+    result = {"kernel_sources_sha256": kernel_sources_hash(), "copy_mib": copy_mib,
+              "fetch_scale": f_scale, "write_scale": w_scale, "kernels": {}}
+    lines = ["# HBM traffic per dispatch", "",
+             "FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each scaled by the factor that makes the",
+             "same counter read %d MiB for a plain %d MiB device copy in the same process." % (copy_mib, copy_mib),
+             "", "Commands:", "", "```", cmd_fetch, cmd_write, "```", "",
+             "Scale factors: FETCH %.4f, WRITE %.4f" % (f_scale, w_scale), "",
+             "| kernel | dispatches | FETCH KiB (raw) | WRITE KiB (raw) | read MB | written MB |",
+             "|---|---|---|---|---|---|"]
+    for k in f:
+        if "attn::" not in k:
+            continue
+        fv = f[k].get("FETCH_SIZE", [])
+        wv = w.get(k, {}).get("WRITE_SIZE", [])
+        if not fv or not wv:
+            continue
+        fk = sum(fv) / len(fv)
+        wk = sum(wv) / len(wv)
+        rd = fk * 1024 * f_scale
+        wr = wk * 1024 * w_scale
+        result["kernels"][short(k)] = {"read_bytes": rd, "write_bytes": wr,
+                                       "dispatches": len(fv)}
+        lines.append("| `%s` | %d | %.0f | %.0f | %.1f | %.1f |" % (
+            short(k), len(fv), fk, wk, rd / 1e6, wr / 1e6))
+    if out_json:
+        with open(out_json, "w") as fh:
+            json.dump(result, fh, indent=1, sort_keys=True)
+    return "\n".join(lines) + "\n"
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="what", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("dir")
+    s.add_argument("name")
+    s.add_argument("--cmd", required=True)
+    t = sub.add_parser("traffic")
+    t.add_argument("dir")
+    t.add_argument("fetch_name")
+    t.add_argument("write_name")
+    t.add_argument("--copy-mib", type=int, required=True)
+    t.add_argument("--cmd-fetch", required=True)
+    t.add_argument("--cmd-write", required=True)
+    t.add_argument("--out", default=None)
+    a = ap.parse_args()
+    if a.what == "stats":
+        sys.stdout.write(stats(a.dir, a.name, a.cmd))
+    else:
+        sys.stdout.write(traffic(a.dir, a.fetch_name, a.write_name, a.copy_mib, a.cmd_fetch,
+                                 a.cmd_write, a.out))
+
+
+if __name__ == "__main__":
+    main()
