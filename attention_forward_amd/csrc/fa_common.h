@@ -38,6 +38,12 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 #define ATTN_LDS __attribute__((address_space(3)))
+#ifndef ATTN_KDEPTH
+#define ATTN_KDEPTH 8
+#endif
+#ifndef ATTN_SETPRIO
+#define ATTN_SETPRIO 1
+#endif
 
 // dtype 0: IEEE binary16, dtype 1: bfloat16
 template <int DT>
@@ -137,7 +143,15 @@ __device__ __forceinline__ u32x4 load_b128(__amdgpu_buffer_rsrc_t r, unsigned vo
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0));
 }
 
-__device__ __forceinline__ void vm_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in bits
+// 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).  Issued
+// through the builtin so the compiler's own wait bookkeeping sees it.
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void vm_wait_all() { vm_wait<0>(); }
 
 // ---- LDS operand reads with immediate offsets and data-dependent waits ----
 // The reads are issued through inline asm so that the compiler neither hoists
@@ -186,40 +200,33 @@ __device__ __forceinline__ LaneAddr lane_addresses() {
   return a;
 }
 
-// ---- one 64-key tile for QB blocks of 32 queries owned by this wave ----
+// ---- the three parts of one 64-key tile, for QB blocks of 32 queries ----
 //
-// base: LDS address of the stage (K at +0, V at +TILE_BYTES).  qf: Q^T operands
-// [QB][8] (16-deep d steps).  o: O^T accumulators [4 d-blocks][QB].  m: running
-// max (log2 units, -inf initially); l: this lane's partial running sum (the
-// lane's half of the keys).  key0: global index of the tile's first key;
-// qrow0: global index of this wave's first query.  MASK: apply the key-validity
-// and causal test per score (only tiles that cross the diagonal or the end of
-// the keys; "The FA5090 Optimization Journey", sec. 2.8, mask specialisation).
-// Online softmax across tiles: sec. 2.6 (exp2 with log2 e folded into the
-// scale, running max in the log2 domain), sec. 2.8 (effective max of a fully
-// masked tile); "10 rounds of hand-written fused attention ...", round R8.
-template <int DT, int QB, bool MASK>
-__device__ __forceinline__ void tile_step(unsigned base, const LaneAddr& la,
-                                          const u32x4 (&qf)[QB][8], f32x16 (&o)[4][QB],
-                                          float (&m)[QB], float (&l)[QB], float scale_log2,
-                                          int key0, int qrow0, int n_keys, bool causal,
-                                          int causal_off) {
-  const int lane = threadIdx.x & 63;
-  const int g = lane >> 5;
-  const int n = lane & 31;
+// qf: Q^T operands [QB][8] (16-deep d steps).  s: S^T accumulators [2 key
+// blocks][QB].  o: O^T accumulators [4 d-blocks][QB].  m: reference max (log2
+// units, -inf initially); l: this lane's running sum over its half of the keys.
+// key0: global index of the tile's first key; qrow0: global index of the
+// wave's first query.  Online softmax across tiles: "The FA5090 Optimization
+// Journey", sec. 2.6 (exp2 with log2 e folded into the scale, running max in
+// the log2 domain) and sec. 2.8 (effective max of a fully masked tile); "10
+// rounds of hand-written fused attention ...", round R8 (m and l carried).
 
-  // ---- S^T = K Q^T: 2 key blocks x 8 d-steps, K operands 8 reads ahead ----
-  f32x16 s[2][QB];
+// S^T = K Q^T: 2 key blocks x 8 d-steps; K operands read KD steps ahead.
+// kbase: LDS address of the K tile.
+template <int DT, int QB>
+__device__ __forceinline__ void qk_step(unsigned kbase, const LaneAddr& la,
+                                        const u32x4 (&qf)[QB][8], f32x16 (&s)[2][QB]) {
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) s[kb][qb] = f32x16{};
-  u32x4 ko[8];
+  constexpr int KD = ATTN_KDEPTH;
+  u32x4 ko[KD];
   auto read_k = [&](int i, u32x4& dst) {
     // i = kb * 8 + st
 #define ATTN_KREAD(I)                                                                  \
   case I:                                                                              \
-    dst = lds_b128<((I) >> 3) * 32 * ROW>(base + la.k[(I) & 7]);           \
+    dst = lds_b128<((I) >> 3) * 32 * ROW>(kbase + la.k[(I) & 7]);                     \
     break;
     switch (i) {
       ATTN_KREAD(0) ATTN_KREAD(1) ATTN_KREAD(2) ATTN_KREAD(3) ATTN_KREAD(4) ATTN_KREAD(5)
@@ -229,13 +236,13 @@ __device__ __forceinline__ void tile_step(unsigned base, const LaneAddr& la,
 #undef ATTN_KREAD
   };
 #pragma unroll
-  for (int i = 0; i < 8; ++i) read_k(i, ko[i]);
+  for (int i = 0; i < KD; ++i) read_k(i, ko[i]);
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    u32x4& cur = ko[i & 7];
-    // reads issued so far: min(16, 8 + i); read i is done when at most
+    u32x4& cur = ko[i % KD];
+    // reads issued so far: min(16, KD + i); read i is done when at most
     // (issued - i - 1) younger ones are outstanding
-    switch ((i + 8 < 16 ? 7 : 15 - i)) {
+    switch (i + KD < 16 ? KD - 1 : 15 - i) {
       case 7: lgkm_wait<7>(cur); break;
       case 6: lgkm_wait<6>(cur); break;
       case 5: lgkm_wait<5>(cur); break;
@@ -248,10 +255,31 @@ __device__ __forceinline__ void tile_step(unsigned base, const LaneAddr& la,
     const int kb = i >> 3, st = i & 7;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) s[kb][qb] = mfma<DT>(cur, qf[qb][st], s[kb][qb]);
-    if (i + 8 < 16) read_k(i + 8, ko[i & 7]);
+    if (i + KD < 16) read_k(i + KD, ko[i % KD]);
   }
+}
 
-  // ---- mask (tiles crossing the diagonal / the end of the keys only) ----
+// Online softmax of one S^T tile: scores -> P^T operands pf (rounded to the
+// dtype), rescaled O and updated m, l.  MASK: apply the key-validity and
+// causal test per score (tiles that cross the diagonal or the end of the keys
+// only; "The FA5090 Optimization Journey", sec. 2.8, mask specialisation).
+//
+// Lazy reference max: a lane keeps m unless this tile's max exceeds it by more
+// than TAU (log2 units), so p = exp2(x - m) <= 2^TAU; any finite reference
+// gives the same O = sum p v / sum p and LSE = m + log2 l (the cancelling 1/l
+// of sec. 2.6; the threshold skip of sec. 3).  When m stays, alpha is exactly
+// 1 and the multiply leaves O unchanged.  The multiply itself is unconditional:
+// a branch around it makes the register allocator move the whole accumulator
+// between two homes on every iteration, which costs more than it saves.
+template <int DT, int QB, bool MASK>
+__device__ __forceinline__ void softmax_step(f32x16 (&s)[2][QB], f32x16 (&o)[4][QB],
+                                             float (&m)[QB], float (&l)[QB],
+                                             u32x4 (&pf)[2][2][QB], float scale_log2, int key0,
+                                             int qrow0, int n_keys, bool causal,
+                                             int causal_off) {
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 5;
+  const int n = lane & 31;
   auto hidden = [&](int kb, int qb, int r) {
     const int key = key0 + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
     const int qi = qrow0 + 32 * qb + n;
@@ -266,9 +294,7 @@ __device__ __forceinline__ void tile_step(unsigned base, const LaneAddr& la,
         for (int r = 0; r < 16; ++r)
           if (hidden(kb, qb, r)) s[kb][qb][r] = -INFINITY;
   }
-
-  // ---- online softmax, per query block ----
-  u32x4 pf[2][2][QB];
+  constexpr float TAU = 8.0f;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     float mx = fmaxf(s[0][qb][0], s[0][qb][1]);
@@ -280,11 +306,19 @@ __device__ __forceinline__ void tile_step(unsigned base, const LaneAddr& la,
     // -inf * 0 would be NaN when scale is 0; a fully hidden tile keeps m
     float mxs = mx * scale_log2;
     if constexpr (MASK) mxs = (mx == -INFINITY) ? -INFINITY : mxs;
-    const float m_new = fmaxf(m[qb], mxs);
-    const float m_eff = (m_new == -INFINITY) ? 0.0f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m[qb] - m_eff);
-    m[qb] = m_new;
-    float rs = 0.0f;
+    const bool jump = mxs > m[qb] + TAU;
+    const float alpha =
+        jump ? ((m[qb] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m[qb] - mxs)) : 1.0f;
+    m[qb] = jump ? mxs : m[qb];
+    l[qb] *= alpha;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) o[db][qb] *= alpha;
+    // effective max of a row that has seen no visible key yet ("The FA5090
+    // Optimization Journey", sec. 2.8): exp2(-inf - 0) = 0 keeps it NaN-free
+    const float m_eff = (m[qb] == -INFINITY) ? 0.0f : m[qb];
+    // the row sum adds the fp32 values before they are rounded for the MFMA, so
+    // the LSE is that of the exact weights
+    float rs = l[qb];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -294,12 +328,8 @@ __device__ __forceinline__ void tile_step(unsigned base, const LaneAddr& la,
         s[kb][qb][r] = p;
         rs += p;
       }
-    l[qb] = l[qb] * alpha + rs;
-    // Unconditional: a wave-uniform skip when alpha == 1 ("The FA5090
-    // Optimization Journey", sec. 2.8) makes the compiler copy the whole
-    // accumulator at the branch merge, which costs more than the 64 multiplies.
-#pragma unroll
-    for (int db = 0; db < 4; ++db) o[db][qb] *= alpha;
+    l[qb] = rs;
+    // P rounded to the dtype (RNE) for the MFMA
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -311,19 +341,23 @@ __device__ __forceinline__ void tile_step(unsigned base, const LaneAddr& la,
         pf[kb][t][qb] = w;
       }
   }
+}
 
-  // ---- O^T += V^T P^T: 4 d-blocks x 4 key steps, operands 4 steps ahead ----
-  // step i: db = i >> 2, kb = (i >> 1) & 1, t = i & 1; the operand's two
-  // transposing reads cover keys 32kb + 16t + 4g + {0..3} and the same + 8.
+// O^T += V^T P^T: 4 d-blocks x 4 key steps, operands 4 steps ahead.  Step i:
+// db = i >> 2, kb = (i >> 1) & 1, t = i & 1; the operand's two transposing
+// reads cover keys 32kb + 16t + 4g + {0..3} and the same + 8.  vbase: LDS
+// address of the V tile.
+template <int DT, int QB>
+__device__ __forceinline__ void pv_step(unsigned vbase, const LaneAddr& la,
+                                        const u32x4 (&pf)[2][2][QB], f32x16 (&o)[4][QB]) {
   u32x4 vo[4];
   auto read_v = [&](int i, u32x4& dst) {
     u32x2 lo, hi;
-#define ATTN_VREAD(I)                                                                       \
-  case I:                                                                                   \
-    lo = lds_tr16<TILE_BYTES + (32 * (((I) >> 1) & 1) + 16 * ((I) & 1)) * ROW>(   \
-        base + la.v[(I) >> 2]);                                                             \
-    hi = lds_tr16<TILE_BYTES + (32 * (((I) >> 1) & 1) + 16 * ((I) & 1) + 8) *     \
-                                               ROW>(base + la.v[(I) >> 2]);                 \
+#define ATTN_VREAD(I)                                                                  \
+  case I:                                                                              \
+    lo = lds_tr16<(32 * (((I) >> 1) & 1) + 16 * ((I) & 1)) * ROW>(vbase + la.v[(I) >> 2]); \
+    hi = lds_tr16<(32 * (((I) >> 1) & 1) + 16 * ((I) & 1) + 8) * ROW>(                 \
+        vbase + la.v[(I) >> 2]);                                                       \
     break;
     switch (i) {
       ATTN_VREAD(0) ATTN_VREAD(1) ATTN_VREAD(2) ATTN_VREAD(3) ATTN_VREAD(4) ATTN_VREAD(5)
@@ -350,6 +384,21 @@ __device__ __forceinline__ void tile_step(unsigned base, const LaneAddr& la,
     for (int qb = 0; qb < QB; ++qb) o[db][qb] = mfma<DT>(cur, pf[kb][t][qb], o[db][qb]);
     if (i + 4 < 16) read_v(i + 4, vo[i & 3]);
   }
+}
+
+// The whole tile in one wave: S^T, softmax, O^T.
+template <int DT, int QB, bool MASK>
+__device__ __forceinline__ void tile_step(unsigned kbase, unsigned vbase, const LaneAddr& la,
+                                          const u32x4 (&qf)[QB][8], f32x16 (&o)[4][QB],
+                                          float (&m)[QB], float (&l)[QB], float scale_log2,
+                                          int key0, int qrow0, int n_keys, bool causal,
+                                          int causal_off) {
+  f32x16 s[2][QB];
+  u32x4 pf[2][2][QB];
+  qk_step<DT, QB>(kbase, la, qf, s);
+  softmax_step<DT, QB, MASK>(s, o, m, l, pf, scale_log2, key0, qrow0, n_keys, causal,
+                             causal_off);
+  pv_step<DT, QB>(vbase, la, pf, o);
 }
 
 }  // namespace attn

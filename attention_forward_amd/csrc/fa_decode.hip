@@ -52,6 +52,7 @@ __global__ __launch_bounds__(64, 2) void fa_decode_split_kernel(
     const unsigned row_off = (unsigned)(n * ROW + 16 * g);
 #pragma unroll
     for (int st = 0; st < 8; ++st) qf[0][st] = load_b128(qr, row_off + 32 * st);
+    vm_wait_all();
   }
 
   f32x16 acc[4][1];
@@ -79,9 +80,11 @@ __global__ __launch_bounds__(64, 2) void fa_decode_split_kernel(
     for (int c = 0; c < KT / 4; ++c) load_chunk(vr, voff + c * 4 * ROW, vt + c * 1024);
     vm_wait_all();
     if (key0 + KT > j1)
-      tile_step<DT, 1, true>(base, la, qf, acc, m, l, scale_log2, key0, 0, j1, false, 0);
+      tile_step<DT, 1, true>(base, base + TILE_BYTES, la, qf, acc, m, l, scale_log2, key0, 0,
+                             j1, false, 0);
     else
-      tile_step<DT, 1, false>(base, la, qf, acc, m, l, scale_log2, key0, 0, j1, false, 0);
+      tile_step<DT, 1, false>(base, base + TILE_BYTES, la, qf, acc, m, l, scale_log2, key0, 0,
+                              j1, false, 0);
     // every LDS read of this tile has completed (the MFMAs consumed them)
     // before the next iteration's loads overwrite the stage
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");

@@ -1,37 +1,48 @@
-// Prefill / full forward kernel: one workgroup per (batch*head, block of FWD_BR
-// query rows); FWD_NW waves, each owning FWD_QB blocks of 32 query rows whose
-// Q^T operands stay in registers for the whole key loop.  K and V tiles of 64
-// keys stream HBM -> LDS with direct-to-LDS loads, double buffered so tile j+1
-// is in flight while tile j is consumed ("G5: Pipeline 重构与双缓冲", V21: the
-// load of the next tile overlaps the compute of the current one; "Three kernels
-// for a chip the ecosystem skipped", Kernel one: double-buffered K/V).
+// Prefill / full forward kernel.
 //
-// Causal: only tiles up to the last key visible to the workgroup's last row are
-// loaded; a wave skips the tiles that are fully hidden for all of its rows, and
-// only tiles that cross the diagonal (or the end of the keys) pay for the
-// per-score test ("The FA5090 Optimization Journey", sec. 2.7 causal skip and
-// sec. 2.8 mask specialisation).  Work items are issued heaviest first (largest
-// query block index first), the LPT order of sec. 2.7.
+// One workgroup of 8 waves per (batch*head, block of FWD_BR = 256 query rows);
+// wave w owns rows 32w..32w+31 and keeps their Q^T operands in registers for
+// the whole key loop.  64-key K and V tiles stream HBM -> LDS with
+// bounds-checked direct-to-LDS loads into two rings of two stages each, issued
+// two half-steps before their first use ("G5: Pipeline 重构与双缓冲", V21 and
+// V26: the next tile's load overlaps the current compute, and K and V have
+// separate readiness).
+//
+// Ping-pong: waves w and w+4 share a SIMD.  Group A (waves 0-3) and group B
+// (waves 4-7) alternate between an MFMA phase, [O += P(j-1) V(j-1); S(j) = K(j)
+// Q^T], and a VALU phase, [online softmax of S(j)], one workgroup barrier per
+// half-step, with B one half-step behind A.  So while one wave of a SIMD
+// issues matrix instructions the other runs its exponentials, and the matrix
+// pipe is not left idle while a single wave works through its softmax (the
+// pages' kernels lean on several resident warps for the same overlap: "The
+// FA5090 Optimization Journey", sec. 2.3 and 2.7; "G5", V21).
+//
+// Causal: only tiles up to the last key visible to the workgroup's last row
+// are loaded, a wave computes only the tiles visible to its own rows, and only
+// tiles that cross the diagonal (or the end of the keys) pay for the per-score
+// test ("The FA5090 Optimization Journey", sec. 2.7 causal skip and sec. 2.8
+// mask specialisation).  Work items are issued heaviest first (largest query
+// block first), the LPT order of sec. 2.7.
 #include "fa_common.h"
 #include "launch.h"
 
 namespace attn {
 
-template <int DT, int QB, int NW>
-__global__ __launch_bounds__(NW * 64, FWD_WAVES_PER_SIMD) void fa_fwd_kernel(const uint16_t* __restrict__ q,
-                                                            const uint16_t* __restrict__ k,
-                                                            const uint16_t* __restrict__ v,
-                                                            uint16_t* __restrict__ o,
-                                                            float* __restrict__ lse, int Hq,
-                                                            int Hkv, int Sq, int Sk, int causal,
-                                                            float scale_log2, int n_bh, int n_qt) {
-  constexpr int BR = NW * QB * 32;
-  constexpr int CHUNKS_PER_WAVE = (KT / 4) / NW;  // 1 KiB load instructions per tile per wave
-  static_assert((KT / 4) % NW == 0, "tile rows must split evenly over the waves");
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * 2 * TILE_BYTES];
+template <int DT>
+__global__ __launch_bounds__(FWD_NW * 64, 2) void fa_fwd_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    uint16_t* __restrict__ o, float* __restrict__ lse, int Hq, int Hkv, int Sq, int Sk, int causal,
+    float scale_log2, int n_bh, int n_qt) {
+  constexpr int NW = FWD_NW;
+  constexpr int QB = 1;
+  constexpr int BR = FWD_BR;
+  static_assert(NW == 8 && FWD_QB == 1, "two groups of four single-block waves");
+  // LDS: K stages at [0, 2 tiles), V stages at [2 tiles, 4 tiles)
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * TILE_BYTES];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bool group_a = wave < NW / 2;
   const int g = lane >> 5;
   const int n = lane & 31;
 
@@ -49,7 +60,7 @@ __global__ __launch_bounds__(NW * 64, FWD_WAVES_PER_SIMD) void fa_fwd_kernel(con
   const int causal_off = Sk - Sq;
 
   const int q0 = qt * BR;
-  const int qw0 = q0 + wave * QB * 32;  // this wave's first query row
+  const int qw0 = q0 + wave * 32;  // this wave's first query row
 
   // keys this workgroup needs
   int kv_end = Sk;
@@ -58,78 +69,142 @@ __global__ __launch_bounds__(NW * 64, FWD_WAVES_PER_SIMD) void fa_fwd_kernel(con
     kv_end = min(Sk, max(0, last_q + causal_off + 1));
   }
   const int n_tiles = (kv_end + KT - 1) / KT;
+  // tiles this wave computes: up to its own last visible key, none without rows
+  int n_wave = 0;
+  if (qw0 < Sq) {
+    const int wave_last_q = min(qw0 + 32, Sq) - 1;
+    const int wave_kv_end = causal ? min(Sk, max(0, wave_last_q + causal_off + 1)) : Sk;
+    n_wave = (wave_kv_end + KT - 1) / KT;
+  }
 
   // Q^T operands: lane holds Q[row][16*st + 8*g .. +7] for its query n; rows
   // past Sq read as zeros
   u32x4 qf[QB][8];
   {
     const __amdgpu_buffer_rsrc_t qr = make_rsrc(qh, (long long)Sq * ROW);
+    const unsigned row_off = (unsigned)((qw0 + n) * ROW + 16 * g);
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const unsigned row_off = (unsigned)((qw0 + 32 * qb + n) * ROW + 16 * g);
-#pragma unroll
-      for (int st = 0; st < 8; ++st) qf[qb][st] = load_b128(qr, row_off + 32 * st);
-    }
+    for (int st = 0; st < 8; ++st) qf[0][st] = load_b128(qr, row_off + 32 * st);
+    vm_wait_all();  // Q is in registers before any tile load is issued
   }
+
   f32x16 acc[4][QB];
   float m[QB], l[QB];
+  m[0] = -INFINITY;
+  l[0] = 0.0f;
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    m[qb] = -INFINITY;
-    l[qb] = 0.0f;
-#pragma unroll
-    for (int db = 0; db < 4; ++db) acc[db][qb] = f32x16{};
-  }
+  for (int db = 0; db < 4; ++db) acc[db][0] = f32x16{};
 
-  // lane offsets of this wave's load chunks: chunk c*NW + wave covers rows
-  // 16c + 4*wave + lane/16, so the swizzle pattern is the same for every c
-  static_assert(NW == 4, "one lane offset per wave needs chunks 16 rows apart");
-  const unsigned koff = load_lane_offset<false>(wave);
-  const unsigned voff = load_lane_offset<true>(wave);
-  auto issue_tile = [&](int j) {
-    unsigned char ATTN_LDS* base = (unsigned char ATTN_LDS*)(smem) + (j & 1) * 2 * TILE_BYTES;
+  // Group A (4 waves) loads every tile: chunk 4c + wave covers rows
+  // 16c + 4*wave + lane/16, one swizzle pattern (and so one lane offset) per
+  // wave for every chunk
+  constexpr int LOADERS = NW / 2;
+  constexpr int CHUNKS_PER_LOADER = (KT / 4) / LOADERS;
+  const unsigned koff = load_lane_offset<false>(wave & (LOADERS - 1));
+  const unsigned voff = load_lane_offset<true>(wave & (LOADERS - 1));
+  unsigned char ATTN_LDS* lds = (unsigned char ATTN_LDS*)(smem);
+  auto issue = [&](const uint16_t* head, unsigned lane_off, int j, unsigned char ATTN_LDS* dst) {
     const int key0 = j * KT;
-    const long long bytes = (long long)(Sk - key0) * ROW;  // keys past Sk read as zeros
-    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kh + (size_t)key0 * D, bytes);
-    const __amdgpu_buffer_rsrc_t vr = make_rsrc(vh + (size_t)key0 * D, bytes);
+    // keys past Sk read as zeros
+    const __amdgpu_buffer_rsrc_t r =
+        make_rsrc(head + (size_t)key0 * D, (long long)(Sk - key0) * ROW);
 #pragma unroll
-    for (int c = 0; c < CHUNKS_PER_WAVE; ++c)
-      load_chunk(kr, koff + c * 16 * ROW, base + (c * NW + wave) * 1024);
-#pragma unroll
-    for (int c = 0; c < CHUNKS_PER_WAVE; ++c)
-      load_chunk(vr, voff + c * 16 * ROW, base + TILE_BYTES + (c * NW + wave) * 1024);
+    for (int c = 0; c < CHUNKS_PER_LOADER; ++c)
+      load_chunk(r, lane_off + c * LOADERS * 4 * ROW, dst + (c * LOADERS + wave) * 1024);
+  };
+  auto k_stage = [&](int j) { return lds + (j & 1) * TILE_BYTES; };
+  auto v_stage = [&](int j) { return lds + (2 + (j & 1)) * TILE_BYTES; };
+  const LaneAddr la = lane_addresses();
+  const unsigned lds_base = (unsigned)(size_t)lds;
+
+  f32x16 s[2][QB];
+  u32x4 pf[2][2][QB];
+
+  // Every wave runs the same sequence  [MFMA(j)] barrier [softmax(j)] barrier,
+  // group B one barrier later than group A, so each half-step pairs A's MFMA
+  // phase with B's softmax phase and vice versa.  Group A issues K(j+1) and
+  // V(j) at the start of its step j and waits for them at its end: their
+  // stages were last read by B's MFMA phase of step j-1, which ends before the
+  // barrier A passes to start step j, and they are next read by A's MFMA phase
+  // of step j+1.
+  // group A's loads of step j and the wait for them, at the start and the end
+  auto loads = [&](int j) {
+    if (group_a) {
+      if (j + 1 < n_tiles) issue(kh, koff, j + 1, k_stage(j + 1));
+      if (j < n_tiles) issue(vh, voff, j, v_stage(j));
+    }
+  };
+  auto landed = [&]() {
+    if (group_a) vm_wait_all();  // K(j+1), V(j) have landed
+  };
+  auto barrier = [] { __builtin_amdgcn_s_barrier(); };
+  auto k_addr = [&](int j) { return lds_base + (unsigned)((j & 1) * TILE_BYTES); };
+  auto v_addr = [&](int j) { return lds_base + (unsigned)((2 + (j & 1)) * TILE_BYTES); };
+  auto softmax = [&](int j) {
+    const int key0 = j * KT;
+    if ((key0 + KT > Sk) || (causal && key0 + KT - 1 > qw0 + causal_off))
+      softmax_step<DT, QB, true>(s, acc, m, l, pf, scale_log2, key0, qw0, Sk, causal != 0,
+                                 causal_off);
+    else
+      softmax_step<DT, QB, false>(s, acc, m, l, pf, scale_log2, key0, qw0, Sk, false, 0);
+  };
+  auto prio_hi = [] {
+    if (ATTN_SETPRIO) __builtin_amdgcn_s_setprio(1);
+  };
+  auto prio_lo = [] {
+    if (ATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
   };
 
-  const int wave_last_q = min(qw0 + QB * 32, Sq) - 1;
-  const bool wave_active = qw0 < Sq;
-  const LaneAddr la = lane_addresses();
-  const unsigned smem_base = (unsigned)(size_t)(unsigned char ATTN_LDS*)(smem);
-
-  if (n_tiles > 0) issue_tile(0);
-  for (int j = 0; j < n_tiles; ++j) {
-    vm_wait_all();
-    __syncthreads();
-    if (j + 1 < n_tiles) issue_tile(j + 1);
-    const int key0 = j * KT;
-    const bool hidden = causal && key0 > wave_last_q + causal_off;
-    if (wave_active && !hidden) {
-      const bool need_mask =
-          (key0 + KT > Sk) || (causal && key0 + KT - 1 > qw0 + causal_off);
-      const unsigned base = smem_base + (unsigned)((j & 1) * 2 * TILE_BYTES);
-      if (need_mask)
-        tile_step<DT, QB, true>(base, la, qf, acc, m, l, scale_log2, key0, qw0, Sk, causal != 0,
-                                causal_off);
-      else
-        tile_step<DT, QB, false>(base, la, qf, acc, m, l, scale_log2, key0, qw0, Sk, false, 0);
+  if (group_a && n_tiles > 0) issue(kh, koff, 0, k_stage(0));
+  vm_wait_all();
+  barrier();
+  if (!group_a) barrier();
+  // The loop is peeled at this wave's first and last computed tile so that
+  // the accumulator is updated unconditionally inside each loop (a path that
+  // skips the update makes the register allocator copy the accumulator).
+  int j = 0;
+  if (n_wave > 0) {
+    loads(0);
+    prio_hi();
+    qk_step<DT, QB>(k_addr(0), la, qf, s);
+    prio_lo();
+    barrier();
+    softmax(0);
+    landed();
+    barrier();
+    for (j = 1; j < n_wave; ++j) {
+      loads(j);
+      prio_hi();
+      pv_step<DT, QB>(v_addr(j - 1), la, pf, acc);
+      qk_step<DT, QB>(k_addr(j), la, qf, s);
+      prio_lo();
+      barrier();
+      softmax(j);
+      landed();
+      barrier();
     }
+    loads(j);
+    prio_hi();
+    pv_step<DT, QB>(v_addr(j - 1), la, pf, acc);
+    prio_lo();
+    barrier();
+    landed();
+    barrier();
+    ++j;
   }
+  for (; j <= n_tiles; ++j) {  // steps with nothing left for this wave
+    loads(j);
+    barrier();
+    landed();
+    barrier();
+  }
+  if (group_a) barrier();
 
   // epilogue: O = acc / l, rounded to the dtype; LSE = ln2 * (m + log2 l)
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const float lt = half_sum(l[qb]);
+  {
+    const float lt = half_sum(l[0]);
     const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
-    const int row = qw0 + 32 * qb + n;
+    const int row = qw0 + n;
     if (row < Sq) {
       uint16_t* orow = o + ((size_t)bh * Sq + row) * D;
 #pragma unroll
@@ -138,13 +213,13 @@ __global__ __launch_bounds__(NW * 64, FWD_WAVES_PER_SIMD) void fa_fwd_kernel(con
         for (int jj = 0; jj < 4; ++jj) {
           const int d0 = 32 * db + 8 * jj + 4 * g;
           u32x2 w;
-          w[0] = pack2<DT>(acc[db][qb][4 * jj + 0] * inv, acc[db][qb][4 * jj + 1] * inv);
-          w[1] = pack2<DT>(acc[db][qb][4 * jj + 2] * inv, acc[db][qb][4 * jj + 3] * inv);
+          w[0] = pack2<DT>(acc[db][0][4 * jj + 0] * inv, acc[db][0][4 * jj + 1] * inv);
+          w[1] = pack2<DT>(acc[db][0][4 * jj + 2] * inv, acc[db][0][4 * jj + 3] * inv);
           *reinterpret_cast<u32x2*>(orow + d0) = w;
         }
       if (lse != nullptr && g == 0)
         lse[(size_t)bh * Sq + row] =
-            lt > 0.0f ? 0.69314718055994531f * (m[qb] + __builtin_amdgcn_logf(lt)) : -INFINITY;
+            lt > 0.0f ? 0.69314718055994531f * (m[0] + __builtin_amdgcn_logf(lt)) : -INFINITY;
     }
   }
 }
@@ -159,11 +234,11 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
   auto v = static_cast<const uint16_t*>(a.v);
   auto o = static_cast<uint16_t*>(a.o);
   if (a.dtype == 0)
-    hipLaunchKernelGGL((fa_fwd_kernel<0, FWD_QB, FWD_NW>), grid, block, 0, stream, q, k, v, o,
-                       a.lse, a.Hq, a.Hkv, a.Sq, a.Sk, a.causal, a.scale_log2, n_bh, n_qt);
+    hipLaunchKernelGGL((fa_fwd_kernel<0>), grid, block, 0, stream, q, k, v, o, a.lse, a.Hq,
+                       a.Hkv, a.Sq, a.Sk, a.causal, a.scale_log2, n_bh, n_qt);
   else
-    hipLaunchKernelGGL((fa_fwd_kernel<1, FWD_QB, FWD_NW>), grid, block, 0, stream, q, k, v, o,
-                       a.lse, a.Hq, a.Hkv, a.Sq, a.Sk, a.causal, a.scale_log2, n_bh, n_qt);
+    hipLaunchKernelGGL((fa_fwd_kernel<1>), grid, block, 0, stream, q, k, v, o, a.lse, a.Hq,
+                       a.Hkv, a.Sq, a.Sk, a.causal, a.scale_log2, n_bh, n_qt);
   return hipGetLastError();
 }
 

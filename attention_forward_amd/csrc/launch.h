@@ -52,11 +52,15 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 #define ATTN_FWD_QB 1
 #endif
 #ifndef ATTN_FWD_NW
-#define ATTN_FWD_NW 4
+#define ATTN_FWD_NW 8
 #endif
 #ifndef ATTN_FWD_WPE
 #define ATTN_FWD_WPE 2
 #endif
+#ifndef ATTN_FWD_STAGES
+#define ATTN_FWD_STAGES 2
+#endif
+constexpr int FWD_STAGES = ATTN_FWD_STAGES;  // K/V tiles resident in LDS per workgroup
 constexpr int FWD_QB = ATTN_FWD_QB;
 constexpr int FWD_NW = ATTN_FWD_NW;
 constexpr int FWD_WAVES_PER_SIMD = ATTN_FWD_WPE;  // occupancy the register budget is sized for
