@@ -4,8 +4,9 @@
 // query slots of the MFMA tile hold the query heads of the kv head's group (up
 // to 32), so each K/V row is read from HBM once for the whole group; the rest
 // of the slots are zero and never stored.  The split's keys stream through a
-// 32 KiB LDS stage (K and V of 64 keys), which lets five such workgroups share
-// a CU and keeps enough bytes in flight for the HBM-bound loop (a
+// 32 KiB LDS stage (K and V of 64 keys) whose K and V halves refill as soon as
+// they have been read, which lets five such workgroups share a CU and keeps
+// bytes in flight for the HBM-bound loop at all times (a
 // matrix-vector product has an arithmetic intensity near 1 FLOP/B, "The FA5090
 // Optimization Journey", sec. 2.3).  The partial output is normalised by its
 // own sum and stored in fp32 with its natural-log LSE.
@@ -52,7 +53,6 @@ __global__ __launch_bounds__(64, 2) void fa_decode_split_kernel(
     const unsigned row_off = (unsigned)(n * ROW + 16 * g);
 #pragma unroll
     for (int st = 0; st < 8; ++st) qf[0][st] = load_b128(qr, row_off + 32 * st);
-    vm_wait_all();
   }
 
   f32x16 acc[4][1];
@@ -70,24 +70,57 @@ __global__ __launch_bounds__(64, 2) void fa_decode_split_kernel(
 #pragma unroll
   for (int c = 0; c < 4; ++c) koff[c] = load_lane_offset<false>(c);
   const unsigned voff = load_lane_offset<true>(0);
+  // K and V stages refill independently: K(t+1) is issued as soon as QK(t)
+  // has read the K stage and V(t+1) as soon as PV(t) has read the V stage, so
+  // the next tile's bytes are in flight while this tile is computed.  Loads
+  // complete in issue order (K(t), V(t), K(t+1), V(t+1), ...), so "K(t) has
+  // landed" is vmcnt <= one tile half (V(t)) and "V(t) has landed" is
+  // vmcnt <= one tile half (K(t+1)) or 0 on the last tile.
+  constexpr int HALF = KT / 4;  // load instructions per K or V tile
+  auto issue_k = [&](int key0) {
+    // keys past the split read as zeros
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(kh + (size_t)key0 * D, (long long)(j1 - key0) * ROW);
+#pragma unroll
+    for (int c = 0; c < HALF; ++c) load_chunk(r, koff[c & 3] + (c >> 2) * 16 * ROW, kt + c * 1024);
+  };
+  auto issue_v = [&](int key0) {
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(vh + (size_t)key0 * D, (long long)(j1 - key0) * ROW);
+#pragma unroll
+    for (int c = 0; c < HALF; ++c) load_chunk(r, voff + c * 4 * ROW, vt + c * 1024);
+  };
+  // every LDS read issued so far has returned (the stage may be overwritten)
+  auto lds_drained = [] { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); };
+  if (j0 < j1) {
+    issue_k(j0);
+    issue_v(j0);
+    // Q has landed; K(0) and V(0) may still be in flight.  Tying Q's registers
+    // to the wait keeps it after the tile loads and tells the compiler that Q is
+    // ready, so it does not wait for every load before the loop.
+    asm volatile("s_waitcnt vmcnt(%8)"
+                 : "+v"(qf[0][0]), "+v"(qf[0][1]), "+v"(qf[0][2]), "+v"(qf[0][3]),
+                   "+v"(qf[0][4]), "+v"(qf[0][5]), "+v"(qf[0][6]), "+v"(qf[0][7])
+                 : "n"(2 * HALF)
+                 : "memory");
+  }
   for (int key0 = j0; key0 < j1; key0 += KT) {
-    const long long bytes = (long long)(j1 - key0) * ROW;  // keys past the split read as zeros
-    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kh + (size_t)key0 * D, bytes);
-    const __amdgpu_buffer_rsrc_t vr = make_rsrc(vh + (size_t)key0 * D, bytes);
-#pragma unroll
-    for (int c = 0; c < KT / 4; ++c) load_chunk(kr, koff[c & 3] + (c >> 2) * 16 * ROW, kt + c * 1024);
-#pragma unroll
-    for (int c = 0; c < KT / 4; ++c) load_chunk(vr, voff + c * 4 * ROW, vt + c * 1024);
-    vm_wait_all();
+    const bool more = key0 + KT < j1;
+    f32x16 s[2][1];
+    u32x4 pf[2][2][1];
+    vm_wait<HALF>();  // K(t)
+    qk_step<DT, 1>(base, la, qf, s);
+    lds_drained();
+    if (more) issue_k(key0 + KT);
     if (key0 + KT > j1)
-      tile_step<DT, 1, true>(base, base + TILE_BYTES, la, qf, acc, m, l, scale_log2, key0, 0,
-                             j1, false, 0);
+      softmax_step<DT, 1, true>(s, acc, m, l, pf, scale_log2, key0, 0, j1, false, 0);
     else
-      tile_step<DT, 1, false>(base, base + TILE_BYTES, la, qf, acc, m, l, scale_log2, key0, 0,
-                              j1, false, 0);
-    // every LDS read of this tile has completed (the MFMAs consumed them)
-    // before the next iteration's loads overwrite the stage
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      softmax_step<DT, 1, false>(s, acc, m, l, pf, scale_log2, key0, 0, j1, false, 0);
+    if (more)
+      vm_wait<HALF>();  // V(t); K(t+1) may be in flight
+    else
+      vm_wait_all();
+    pv_step<DT, 1>(base + TILE_BYTES, la, pf, acc);
+    lds_drained();
+    if (more) issue_v(key0 + KT);
   }
 
   const float lt = half_sum(l[0]);
