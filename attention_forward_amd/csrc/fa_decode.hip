@@ -143,35 +143,68 @@ __global__ __launch_bounds__(64, 2) void fa_decode_split_kernel(
   }
 }
 
-// One workgroup of D threads per (batch, query head); thread c owns column c.
+// One wave per (batch, query head) row, COMBINE_ROWS rows per workgroup; lane
+// c owns columns 2c and 2c+1.  Splits are merged COMBINE_BLOCK at a time with
+// the online-softmax rescale (running max M, running sum L): a block's partial
+// LSEs (wave-uniform, scalar loads) and partial outputs are loaded together, so
+// a row costs one memory round trip per block rather than a max pass followed
+// by a weighted-sum pass.
+constexpr int COMBINE_ROWS = 4;
+constexpr int COMBINE_BLOCK = 16;
+static_assert(D == 128, "a wave covers one row of 128 columns, two per lane");
+
 template <int DT>
-__global__ __launch_bounds__(D) void fa_combine_kernel(const float* __restrict__ o_part,
-                                                        const float* __restrict__ lse_part,
-                                                        uint16_t* __restrict__ o,
-                                                        float* __restrict__ lse, int num_splits) {
-  const int r = blockIdx.x;
-  const int c = threadIdx.x;
+__global__ __launch_bounds__(64 * COMBINE_ROWS) void fa_combine_kernel(
+    const float* __restrict__ o_part, const float* __restrict__ lse_part,
+    uint16_t* __restrict__ o, float* __restrict__ lse, int rows, int num_splits) {
+  const int lane = threadIdx.x & 63;
+  const unsigned r = blockIdx.x * COMBINE_ROWS + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (r >= (unsigned)rows) return;
   const float* ls = lse_part + (size_t)r * num_splits;
-  float M = -INFINITY;
-  for (int s = 0; s < num_splits; ++s) M = fmaxf(M, ls[s]);
-  float out = 0.0f, L = 0.0f;
-  if (M != -INFINITY) {
-    float accum = 0.0f;
-    for (int s = 0; s < num_splits; ++s) {
-      const float w = __expf(ls[s] - M);  // exp(-inf) = 0 for empty splits
+  const float* op = o_part + (size_t)r * num_splits * D + 2 * lane;
+  float M = -INFINITY, L = 0.0f, a0 = 0.0f, a1 = 0.0f;
+  // merge n splits starting at s whose LSEs are lv and outputs x
+  auto merge = [&](const float* lv, const float2* x, int n) {
+    float mb = -INFINITY;
+    for (int i = 0; i < n; ++i) mb = fmaxf(mb, lv[i]);
+    const float mn = fmaxf(M, mb);
+    // while every split so far is empty (mn = -inf) shift by 0: every weight
+    // is then exp(-inf) = 0, with no branch that would hold back the loads
+    const float ref = mn == -INFINITY ? 0.0f : mn;
+    const float alpha = __expf(M - ref);  // 0 while M = -inf
+    L *= alpha;
+    a0 *= alpha;
+    a1 *= alpha;
+    for (int i = 0; i < n; ++i) {
+      const float w = __expf(lv[i] - ref);  // exp(-inf) = 0 for an empty split
       L += w;
-      accum += w * o_part[((size_t)r * num_splits + s) * D + c];
+      a0 += w * x[i].x;
+      a1 += w * x[i].y;
     }
-    out = accum / L;
+    M = mn;
+  };
+  int s = 0;
+  for (; s + COMBINE_BLOCK <= num_splits; s += COMBINE_BLOCK) {
+    float lv[COMBINE_BLOCK];
+    float2 x[COMBINE_BLOCK];
+#pragma unroll
+    for (int i = 0; i < COMBINE_BLOCK; ++i)
+      x[i] = *reinterpret_cast<const float2*>(op + (size_t)(s + i) * D);
+#pragma unroll
+    for (int i = 0; i < COMBINE_BLOCK; ++i) lv[i] = ls[s + i];
+    merge(lv, x, COMBINE_BLOCK);
   }
-  if constexpr (DT == 0) {
-    _Float16 h = (_Float16)out;
-    o[(size_t)r * D + c] = __builtin_bit_cast(uint16_t, h);
-  } else {
-    __bf16 h = (__bf16)out;
-    o[(size_t)r * D + c] = __builtin_bit_cast(uint16_t, h);
+  for (; s < num_splits; ++s) {
+    const float lv = ls[s];
+    const float2 x = *reinterpret_cast<const float2*>(op + (size_t)s * D);
+    merge(&lv, &x, 1);
   }
-  if (lse != nullptr && c == 0) lse[r] = (M == -INFINITY) ? -INFINITY : M + __logf(L);
+  if (L > 0.0f) {
+    a0 /= L;
+    a1 /= L;
+  }
+  *reinterpret_cast<unsigned*>(o + (size_t)r * D + 2 * lane) = pack2<DT>(a0, a1);
+  if (lse != nullptr && lane == 0) lse[r] = (M == -INFINITY) ? -INFINITY : M + __logf(L);
 }
 
 hipError_t launch_decode_split(const DecodeArgs& a, hipStream_t stream) {
@@ -190,14 +223,14 @@ hipError_t launch_decode_split(const DecodeArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
-  dim3 grid((unsigned)a.rows), block(D);
+  dim3 grid((unsigned)((a.rows + COMBINE_ROWS - 1) / COMBINE_ROWS)), block(64 * COMBINE_ROWS);
   auto o = static_cast<uint16_t*>(a.o);
   if (a.dtype == 0)
     hipLaunchKernelGGL((fa_combine_kernel<0>), grid, block, 0, stream, a.o_part, a.lse_part, o,
-                       a.lse, a.num_splits);
+                       a.lse, a.rows, a.num_splits);
   else
     hipLaunchKernelGGL((fa_combine_kernel<1>), grid, block, 0, stream, a.o_part, a.lse_part, o,
-                       a.lse, a.num_splits);
+                       a.lse, a.rows, a.num_splits);
   return hipGetLastError();
 }
 

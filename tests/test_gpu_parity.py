@@ -175,6 +175,7 @@ DECODE_SMALL = [
     (3, 16, 2, 64, 64, BF16),
     (1, 4, 2, 10, 8, F16),
     (2, 12, 4, 777, 5, BF16),
+    (2, 8, 8, 40, 32, F16),  # splits 20..31 hold no keys
 ]
 
 
@@ -196,14 +197,18 @@ def test_decode_small(shape):
 
 
 @pytest.mark.parametrize("dtype", [F16, BF16])
-def test_combine_matches_oracle(dtype):
-    say("case combine", dtype)
-    rng = np.random.default_rng(5)
-    B, Hq, S = 3, 5, 11
+@pytest.mark.parametrize("S", [11, 16, 37, 70])
+def test_combine_matches_oracle(dtype, S):
+    """Split counts below, at and past whole blocks of merged splits, and past 64."""
+    say("case combine", dtype, S)
+    rng = np.random.default_rng(5 + S)
+    B, Hq = 3, 5
     o_part = rng.standard_normal((B, Hq, S, 128))
     lse_part = rng.standard_normal((B, Hq, S)) * 3
     lse_part[0, 0, 3:] = -np.inf          # some empty splits
     lse_part[1, 2, :] = -np.inf           # a row with no keys at all
+    lse_part[2, 1, :min(S - 1, 20)] = -np.inf  # leading empty splits, then keys
+    lse_part[2, 3, -1] = 40.0             # one split dominates the rest
     o_part[lse_part == -np.inf] = 0.0
     o_part = o_part.astype(np.float32).astype(np.float64)
     lse_part = lse_part.astype(np.float32).astype(np.float64)
