@@ -1,4 +1,5 @@
-"""Build libattn.so (the gfx950 kernels and their C ABI) in-tree with hipcc.
+"""Build libattn.so (the gfx950 kernels and their C ABI) in-tree with hipcc, and
+libattn_bench.so (the benchmark's HBM read-stream probe, csrc_bench/).
 
     python -m attention_forward_amd.build            # build
     python -m attention_forward_amd.build --asm DIR  # also keep the gfx950 assembly
@@ -15,6 +16,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libattn.so")
+CSRC_BENCH = os.path.join(HERE, "csrc_bench")
+LIB_BENCH = os.path.join(HERE, "libattn_bench.so")
 ARCH = "gfx950"
 
 
@@ -39,10 +42,9 @@ def flags():
     ]
 
 
-def build(asm_dir: str | None = None, verbose: bool = False) -> str:
-    cc = hipcc()
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [cc] + flags() + ["-shared", "-o", tmp] + sources()
+def _link(cc, srcs, out, verbose):
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = [cc] + flags() + ["-shared", "-o", tmp] + srcs
     if verbose:
         print(" ".join(cmd))
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -53,7 +55,13 @@ def build(asm_dir: str | None = None, verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + err)
     if err.strip() and verbose:
         print(err)
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(asm_dir: str | None = None, verbose: bool = False) -> str:
+    cc = hipcc()
+    _link(cc, sources(), LIB, verbose)
+    _link(cc, sorted(glob.glob(os.path.join(CSRC_BENCH, "*.hip"))), LIB_BENCH, verbose)
     if asm_dir:
         os.makedirs(asm_dir, exist_ok=True)
         for src in sources():

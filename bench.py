@@ -10,9 +10,11 @@ One step is one pass of the whole hot path over one batch of synthetic input:
 Inputs are seeded N(0,1) values already resident in HBM when the timed region
 starts.  Kernel durations come from HIP events recorded on the stream the
 library launches on (torch's current stream).  `value` is the prefill
-throughput in TFLOP/s; the decode rate, a GEMM ceiling measured on the same
-GPU, the roofline of the dominant kernel and the FP64 CPU oracle timed on a
-bounded sample of the prefill workload are reported beside it.  The oracle's
+throughput in TFLOP/s; the decode rate, GEMM ceilings (square and
+attention-shaped batched) and an HBM read-stream ceiling measured on the same
+GPU, the other prefill workloads, the roofline of the dominant kernel and the
+FP64 CPU oracle timed on a bounded sample of the prefill workload are reported
+beside it.  The oracle's
 sample also checks the GPU output on those rows; a failing check prints no
 throughput.
 
@@ -57,22 +59,29 @@ def decode_algorithmic_bytes(w) -> int:
     return kv + q + o + lse
 
 
-def measured_traffic():
+def measured_traffic(path=None):
     """HBM bytes per launch of the prefill and decode kernels from the committed
     rocprofv3 counter summary (profiles/traffic.json), or None for a kernel
     whose sources changed since the counters were taken."""
     from attention_forward_amd.profsum import kernel_sources_hash
 
-    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "traffic.json")
+    if path is None:
+        path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                            "traffic.json")
     if not os.path.exists(path):
         return None, None
     t = json.load(open(path))
     if t.get("kernel_sources_sha256") != kernel_sources_hash():
         return None, None
     k = t["kernels"]
-    fwd = k.get("attn::fa_fwd_kernel<1, 1, 4>")
-    split = k.get("attn::fa_decode_split_kernel<1>")
-    comb = k.get("attn::fa_combine_kernel<1>")
+
+    def find(prefix):  # the bf16 instantiation of a kernel template
+        hits = [v for name, v in k.items() if name.startswith(prefix)]
+        return hits[0] if len(hits) == 1 else None
+
+    fwd = find("attn::fa_fwd_kernel<1")
+    split = find("attn::fa_decode_split_kernel<1")
+    comb = find("attn::fa_combine_kernel<1")
     pre = None if fwd is None else {"bytes": round(fwd["read_bytes"] + fwd["write_bytes"]),
                                     "read": round(fwd["read_bytes"]),
                                     "write": round(fwd["write_bytes"])}
@@ -82,6 +91,88 @@ def measured_traffic():
         wr = split["write_bytes"] + comb["write_bytes"]
         dec = {"bytes": round(rd + wr), "read": round(rd), "write": round(wr)}
     return pre, dec
+
+
+def _time_ms(fn, iters, warmup=3):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(iters):
+        fn()
+    e.record()
+    e.synchronize()
+    return s.elapsed_time(e) / iters
+
+
+def bmm_ceiling(dtype=torch.bfloat16, bh=32, n=8192, d=128, iters=10):
+    """The attention-shaped product S = Q K^T of the headline workload as one
+    batched GEMM ([32, 8192, 128] x [32, 128, 8192], both operands contiguous)."""
+    a = torch.randn(bh, n, d, device="cuda", dtype=dtype)
+    b = torch.randn(bh, d, n, device="cuda", dtype=dtype)
+    c = torch.empty(bh, n, n, device="cuda", dtype=dtype)
+    ms = _time_ms(lambda: torch.bmm(a, b, out=c), iters)
+    del a, b, c
+    return 2.0 * bh * n * n * d / (ms * 1e-3) / 1e12
+
+
+def hbm_read_ceiling(gib=4, iters=10):
+    """Best read rate of a plain streaming kernel (libattn_bench.so) over a few
+    launch shapes; returns (GB/s, shape)."""
+    import ctypes
+
+    lib = ctypes.CDLL(os.path.join(os.path.dirname(A.__file__), "libattn_bench.so"))
+    lib.stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                                ctypes.c_int, ctypes.c_void_p]
+    lib.stream_read.restype = ctypes.c_int
+    nbytes = gib << 30
+    buf = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    best = (0.0, None)
+    for threads, blocks in ((512, 8192), (512, 16384), (512, 32768), (256, 16384)):
+        def run():
+            if lib.stream_read(ctypes.c_void_p(buf.data_ptr()), nbytes,
+                               ctypes.c_void_p(sink.data_ptr()), blocks, threads, stream) != 0:
+                raise RuntimeError("stream_read launch failed")
+        gbs = nbytes / (_time_ms(run, iters) * 1e-3) / 1e9
+        if gbs > best[0]:
+            best = (gbs, "%d x %d threads" % (blocks, threads))
+    del buf, sink
+    return best
+
+
+def other_workloads(iters=5):
+    """Prefill TFLOP/s of the other prefill workloads (context; their parity is
+    checked by the GPU tests)."""
+    out = {}
+    for name, w in WORKLOADS.items():
+        if w.decode or w is PREFILL:
+            continue
+        q, k, v = [t.cuda() for t in make_workload_inputs(w)]
+        o = torch.empty_like(q)
+        lse = torch.empty(q.shape[:3], device="cuda", dtype=torch.float32)
+        ms = _time_ms(lambda: A.attn_fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse),
+                      iters, warmup=2)
+        out[name] = {"ms": round(ms, 4), "tflops": round(w.flops / (ms * 1e-3) / 1e12, 2)}
+        del q, k, v, o, lse
+    return out
+
+
+def ratio(a, b):
+    """a / b rounded, or None when the ceiling b was not measured."""
+    return None if b is None or not math.isfinite(b) else round(a / b, 4)
+
+
+def spread(xs):
+    """median, p10 and p90 of a list of durations (ms)."""
+    t = sorted(xs)
+
+    def pct(p):
+        return t[min(len(t) - 1, int(round(p * (len(t) - 1))))]
+
+    return {"median": round(pct(0.5), 4), "p10": round(pct(0.1), 4), "p90": round(pct(0.9), 4)}
 
 
 def gemm_ceiling(dtype, n=8192, iters=20):
@@ -158,8 +249,9 @@ def main():
                     help="target wall time of the oracle's CPU-baseline sample")
     ap.add_argument("--skip-cpu-baseline", action="store_true",
                     help="for profiler runs: no oracle leg (and no parity rows)")
-    ap.add_argument("--skip-gemm", action="store_true",
-                    help="for profiler runs: do not measure the GEMM ceiling")
+    ap.add_argument("--skip-context", "--skip-gemm", dest="skip_context", action="store_true",
+                    help="for profiler runs: measure no ceilings (GEMM, batched GEMM, HBM read "
+                         "stream) and no other workloads, so only the step's kernels run")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the timed region, run one plain device copy of this many MiB "
                          "(a known-size kernel for scaling HBM byte counters)")
@@ -223,13 +315,18 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    if args.skip_gemm:
+    if args.skip_context:
         gemm = {}
         gemm_best = float("nan")
+        stream_gbs, stream_shape = float("nan"), None
+        others = {}
     else:
         gemm = {"bf16_8192^3": round(gemm_ceiling(torch.bfloat16), 1),
-                "fp16_8192^3": round(gemm_ceiling(torch.float16), 1)}
+                "fp16_8192^3": round(gemm_ceiling(torch.float16), 1),
+                "bf16_bmm_32x8192x8192x128": round(bmm_ceiling(), 1)}
         gemm_best = max(gemm.values())
+        stream_gbs, stream_shape = hbm_read_ceiling()
+        others = other_workloads()
 
     traffic_pre, traffic_dec = measured_traffic()
     result = {
@@ -254,14 +351,21 @@ def main():
                        "d": DECODE.d, "num_splits": DECODE.num_splits},
             "parallelism": "none (1 GPU)",
         },
-        "prefill": {"ms": round(pre_avg, 4), "tflops": round(tflops, 2),
+        "prefill": {"ms": round(pre_avg, 4), "ms_spread": spread(pre_ms),
+                    "tflops": round(tflops, 2),
                     "frac_mfma_peak": round(tflops / PEAK_MFMA_TFLOPS, 4),
-                    "frac_gemm_ceiling": round(tflops / gemm_best, 4),
+                    "frac_gemm_ceiling": ratio(tflops, gemm_best),
                     "flops": PREFILL.flops, "exp2_per_launch": PREFILL.flops // (4 * PREFILL.d)},
-        "decode": {"ms": round(dec_avg, 4), "value": round(dec_gbs, 1), "unit": "GB/s",
+        "decode": {"ms": round(dec_avg, 4), "ms_spread": spread(dec_ms),
+                   "value": round(dec_gbs, 1), "unit": "GB/s",
                    "frac_hbm_peak": round(dec_gbs / PEAK_HBM_GBS, 4),
+                   "frac_read_stream_ceiling": ratio(dec_gbs, stream_gbs),
                    "algorithmic_bytes": dec_bytes},
         "gemm_ceiling_tflops": gemm,
+        "hbm_read_stream_ceiling": {"value": None if stream_shape is None else round(stream_gbs, 1),
+                                    "unit": "GB/s",
+                                    "shape": stream_shape, "bytes": 4 << 30},
+        "other_workloads": others,
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_MFMA_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_MFMA_TFLOPS, 4),
                      "traffic": None if traffic_pre is None else traffic_pre["bytes"],
