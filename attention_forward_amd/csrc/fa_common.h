@@ -271,12 +271,19 @@ __device__ __forceinline__ void qk_step(unsigned kbase, const LaneAddr& la,
 // 1 and the multiply leaves O unchanged.  The multiply itself is unconditional:
 // a branch around it makes the register allocator move the whole accumulator
 // between two homes on every iteration, which costs more than it saves.
-template <int DT, int QB, bool MASK>
-__device__ __forceinline__ void softmax_step(f32x16 (&s)[2][QB], f32x16 (&o)[4][QB],
+//
+// RESCALE_O = false leaves O alone and instead reports, as the return value,
+// whether any lane of the wave moved a finite reference max (the only case in
+// which O must be multiplied by alpha: a row whose max was -inf has O = 0).
+// The caller then applies alpha itself; until that happens alpha is exactly 1
+// for every lane, so skipping the multiply changes no bit.
+template <int DT, int QB, bool MASK, bool RESCALE_O = true>
+__device__ __forceinline__ bool softmax_step(f32x16 (&s)[2][QB], f32x16 (&o)[4][QB],
                                              float (&m)[QB], float (&l)[QB],
                                              u32x4 (&pf)[2][2][QB], float scale_log2, int key0,
-                                             int qrow0, int n_keys, bool causal,
-                                             int causal_off) {
+                                             int qrow0, int n_keys, bool causal, int causal_off,
+                                             float (&alpha_out)[QB]) {
+  bool moved = false;
   const int lane = threadIdx.x & 63;
   const int g = lane >> 5;
   const int n = lane & 31;
@@ -309,10 +316,14 @@ __device__ __forceinline__ void softmax_step(f32x16 (&s)[2][QB], f32x16 (&o)[4][
     const bool jump = mxs > m[qb] + TAU;
     const float alpha =
         jump ? ((m[qb] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m[qb] - mxs)) : 1.0f;
+    moved |= jump && m[qb] != -INFINITY;
     m[qb] = jump ? mxs : m[qb];
     l[qb] *= alpha;
+    alpha_out[qb] = alpha;
+    if constexpr (RESCALE_O) {
 #pragma unroll
-    for (int db = 0; db < 4; ++db) o[db][qb] *= alpha;
+      for (int db = 0; db < 4; ++db) o[db][qb] *= alpha;
+    }
     // effective max of a row that has seen no visible key yet ("The FA5090
     // Optimization Journey", sec. 2.8): exp2(-inf - 0) = 0 keeps it NaN-free
     const float m_eff = (m[qb] == -INFINITY) ? 0.0f : m[qb];
@@ -341,6 +352,10 @@ __device__ __forceinline__ void softmax_step(f32x16 (&s)[2][QB], f32x16 (&o)[4][
         pf[kb][t][qb] = w;
       }
   }
+  if constexpr (RESCALE_O)
+    return false;
+  else
+    return __builtin_amdgcn_ballot_w64(moved) != 0;
 }
 
 // O^T += V^T P^T: 4 d-blocks x 4 key steps, operands 4 steps ahead.  Step i:
@@ -396,8 +411,9 @@ __device__ __forceinline__ void tile_step(unsigned kbase, unsigned vbase, const 
   f32x16 s[2][QB];
   u32x4 pf[2][2][QB];
   qk_step<DT, QB>(kbase, la, qf, s);
+  float alpha[QB];
   softmax_step<DT, QB, MASK>(s, o, m, l, pf, scale_log2, key0, qrow0, n_keys, causal,
-                             causal_off);
+                             causal_off, alpha);
   pv_step<DT, QB>(vbase, la, pf, o);
 }
 

@@ -110,10 +110,11 @@ __global__ __launch_bounds__(64, 2) void fa_decode_split_kernel(
     qk_step<DT, 1>(base, la, qf, s);
     lds_drained();
     if (more) issue_k(key0 + KT);
+    float alpha[1];
     if (key0 + KT > j1)
-      softmax_step<DT, 1, true>(s, acc, m, l, pf, scale_log2, key0, 0, j1, false, 0);
+      softmax_step<DT, 1, true>(s, acc, m, l, pf, scale_log2, key0, 0, j1, false, 0, alpha);
     else
-      softmax_step<DT, 1, false>(s, acc, m, l, pf, scale_log2, key0, 0, j1, false, 0);
+      softmax_step<DT, 1, false>(s, acc, m, l, pf, scale_log2, key0, 0, j1, false, 0, alpha);
     if (more)
       vm_wait<HALF>();  // V(t); K(t+1) may be in flight
     else

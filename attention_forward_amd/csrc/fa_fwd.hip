@@ -140,13 +140,29 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fa_fwd_kernel(
   auto barrier = [] { __builtin_amdgcn_s_barrier(); };
   auto k_addr = [&](int j) { return lds_base + (unsigned)((j & 1) * TILE_BYTES); };
   auto v_addr = [&](int j) { return lds_base + (unsigned)((2 + (j & 1)) * TILE_BYTES); };
-  auto softmax = [&](int j) {
+  float alpha[QB];
+  auto masked = [&](int j) {
     const int key0 = j * KT;
-    if ((key0 + KT > Sk) || (causal && key0 + KT - 1 > qw0 + causal_off))
+    return (key0 + KT > Sk) || (causal && key0 + KT - 1 > qw0 + causal_off);
+  };
+  // online softmax of tile j without touching O: returns whether some lane's
+  // finite reference max moved, i.e. whether O must still be scaled by alpha
+  auto softmax_keep_o = [&](int j) {
+    const int key0 = j * KT;
+    if (masked(j))
+      return softmax_step<DT, QB, true, false>(s, acc, m, l, pf, scale_log2, key0, qw0, Sk,
+                                               causal != 0, causal_off, alpha);
+    return softmax_step<DT, QB, false, false>(s, acc, m, l, pf, scale_log2, key0, qw0, Sk,
+                                              false, 0, alpha);
+  };
+  // the same with O scaled by alpha
+  auto softmax_scale_o = [&](int j) {
+    const int key0 = j * KT;
+    if (masked(j))
       softmax_step<DT, QB, true>(s, acc, m, l, pf, scale_log2, key0, qw0, Sk, causal != 0,
-                                 causal_off);
+                                 causal_off, alpha);
     else
-      softmax_step<DT, QB, false>(s, acc, m, l, pf, scale_log2, key0, qw0, Sk, false, 0);
+      softmax_step<DT, QB, false>(s, acc, m, l, pf, scale_log2, key0, qw0, Sk, false, 0, alpha);
   };
   auto prio_hi = [] {
     if (ATTN_SETPRIO) __builtin_amdgcn_s_setprio(1);
@@ -159,9 +175,15 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fa_fwd_kernel(
   vm_wait_all();
   barrier();
   if (!group_a) barrier();
-  // The loop is peeled at this wave's first and last computed tile so that
-  // the accumulator is updated unconditionally inside each loop (a path that
-  // skips the update makes the register allocator copy the accumulator).
+  // The loop is peeled at this wave's first and last computed tile, and the
+  // middle runs in two loops, so that inside each loop the accumulator is
+  // updated unconditionally (a path that skips an update makes the register
+  // allocator copy the accumulator on every iteration).  The first loop never
+  // scales O: with the threshold rule alpha is exactly 1 until some lane's
+  // finite reference max moves, which for most rows never happens after their
+  // first tile.  When it does, O is scaled once and the rest of the tiles run
+  // in the second loop, which scales O on every tile as the recurrence is
+  // written.  The first tile needs no scaling: O is still zero.
   int j = 0;
   if (n_wave > 0) {
     loads(0);
@@ -169,7 +191,7 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fa_fwd_kernel(
     qk_step<DT, QB>(k_addr(0), la, qf, s);
     prio_lo();
     barrier();
-    softmax(0);
+    softmax_keep_o(0);
     landed();
     barrier();
     for (j = 1; j < n_wave; ++j) {
@@ -179,7 +201,24 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fa_fwd_kernel(
       qk_step<DT, QB>(k_addr(j), la, qf, s);
       prio_lo();
       barrier();
-      softmax(j);
+      const bool moved = softmax_keep_o(j);
+      landed();
+      barrier();
+      if (moved) {
+#pragma unroll
+        for (int db = 0; db < 4; ++db) acc[db][0] *= alpha[0];
+        ++j;
+        break;
+      }
+    }
+    for (; j < n_wave; ++j) {
+      loads(j);
+      prio_hi();
+      pv_step<DT, QB>(v_addr(j - 1), la, pf, acc);
+      qk_step<DT, QB>(k_addr(j), la, qf, s);
+      prio_lo();
+      barrier();
+      softmax_scale_o(j);
       landed();
       barrier();
     }

@@ -112,6 +112,27 @@ def test_small_shapes_all_rows(shape):
         assert torch.all(hidden == 0), "fully masked rows must be exactly zero"
 
 
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+@pytest.mark.parametrize("dtype", [F16, BF16], ids=["f16", "bf16"])
+def test_growing_scores_move_the_reference_max(dtype, causal):
+    """Key norms grow sixfold along the sequence, so later tiles' scores pass
+    the first tile's maximum by far more than the rescale threshold: the
+    reference max moves mid-loop and O must be rescaled from then on."""
+    B, H, S = 1, 2, 1000
+    name = "growing scores %s %s" % ("bf16" if dtype else "f16", "causal" if causal else "full")
+    say("case", name)
+    q, k, v = make_qkv(B, H, H, S, S, 128, dtype, seed=77)
+    ramp = torch.linspace(1.0, 6.0, S).view(1, 1, S, 1)
+    k = (k.float() * ramp).to(TORCH_DTYPE[dtype])
+    scale = 1.0 / math.sqrt(128)
+    o_gpu, lse_gpu = gpu_fwd(q, k, v, causal, scale, dtype)
+    o, lse, o_ref = oracle.attention(bits(q), bits(k), bits(v), dtype, causal, scale)
+    n = B * H * S
+    gate(o_gpu.to(torch.float64).numpy().reshape(n, 128), o.reshape(n, 128),
+         o_ref.reshape(n, 128), name=name)
+    check_lse(lse_gpu.to(torch.float64).numpy().reshape(-1), lse.reshape(-1), name)
+
+
 def sample_rows(B, H, S, rng, n_random):
     heads = [0, B * H - 1, int(rng.integers(0, B * H))]
     rows = []
