@@ -95,8 +95,8 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fa_fwd_kernel(
 #pragma unroll
   for (int db = 0; db < 4; ++db) acc[db][0] = f32x16{};
 
-  // Group A (4 waves) loads every tile: chunk 4c + wave covers rows
-  // 16c + 4*wave + lane/16, one swizzle pattern (and so one lane offset) per
+  // One group (4 waves) loads every tile: chunk 4c + w (w = wave & 3) covers
+  // rows 16c + 4w + lane/16, one swizzle pattern (and so one lane offset) per
   // wave for every chunk
   constexpr int LOADERS = NW / 2;
   constexpr int CHUNKS_PER_LOADER = (KT / 4) / LOADERS;
@@ -110,7 +110,8 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fa_fwd_kernel(
         make_rsrc(head + (size_t)key0 * D, (long long)(Sk - key0) * ROW);
 #pragma unroll
     for (int c = 0; c < CHUNKS_PER_LOADER; ++c)
-      load_chunk(r, lane_off + c * LOADERS * 4 * ROW, dst + (c * LOADERS + wave) * 1024);
+      load_chunk(r, lane_off + c * LOADERS * 4 * ROW,
+                 dst + (c * LOADERS + (wave & (LOADERS - 1))) * 1024);
   };
   auto k_stage = [&](int j) { return lds + (j & 1) * TILE_BYTES; };
   auto v_stage = [&](int j) { return lds + (2 + (j & 1)) * TILE_BYTES; };
@@ -127,15 +128,31 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fa_fwd_kernel(
   // stages were last read by B's MFMA phase of step j-1, which ends before the
   // barrier A passes to start step j, and they are next read by A's MFMA phase
   // of step j+1.
-  // group A's loads of step j and the wait for them, at the start and the end
-  auto loads = [&](int j) {
-    if (group_a) {
-      if (j + 1 < n_tiles) issue(kh, koff, j + 1, k_stage(j + 1));
-      if (j < n_tiles) issue(vh, voff, j, v_stage(j));
-    }
+  // The loads of step j, K(j+1) and V(j), are issued at the start of the
+  // half-step in which A runs its MFMA phase j, and have landed by the end of
+  // the next one.  ATTN_LOADER_B selects which group does it: A, at the start
+  // of its MFMA phase and waiting at the end of its softmax phase, or B, at
+  // the start of its softmax phase (of step j-1) and waiting at the end of its
+  // MFMA phase j.  Either way the stages written are free (last read before
+  // the barrier that opens the half-step) and are next read after the barrier
+  // that closes the wait.
+  constexpr bool B_LOADS = ATTN_LOADER_B != 0;
+  const bool loader = B_LOADS ? !group_a : group_a;
+  auto issue_step = [&](int j) {
+    if (j + 1 < n_tiles) issue(kh, koff, j + 1, k_stage(j + 1));
+    if (j < n_tiles) issue(vh, voff, j, v_stage(j));
   };
-  auto landed = [&]() {
-    if (group_a) vm_wait_all();  // K(j+1), V(j) have landed
+  auto mfma_begin = [&](int j) {
+    if (!B_LOADS && group_a) issue_step(j);
+  };
+  auto mfma_end = [&]() {
+    if (B_LOADS && !group_a) vm_wait_all();
+  };
+  auto softmax_begin = [&](int j) {
+    if (B_LOADS && !group_a) issue_step(j + 1);
+  };
+  auto softmax_end = [&]() {
+    if (!B_LOADS && group_a) vm_wait_all();
   };
   auto barrier = [] { __builtin_amdgcn_s_barrier(); };
   auto k_addr = [&](int j) { return lds_base + (unsigned)((j & 1) * TILE_BYTES); };
@@ -171,10 +188,13 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fa_fwd_kernel(
     if (ATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
   };
 
-  if (group_a && n_tiles > 0) issue(kh, koff, 0, k_stage(0));
+  if (loader && n_tiles > 0) issue(kh, koff, 0, k_stage(0));
   vm_wait_all();
   barrier();
-  if (!group_a) barrier();
+  if (!group_a) {
+    softmax_begin(-1);  // the half-step before B's first MFMA phase
+    barrier();
+  }
   // The loop is peeled at this wave's first and last computed tile, and the
   // middle runs in two loops, so that inside each loop the accumulator is
   // updated unconditionally (a path that skips an update makes the register
@@ -186,23 +206,27 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fa_fwd_kernel(
   // written.  The first tile needs no scaling: O is still zero.
   int j = 0;
   if (n_wave > 0) {
-    loads(0);
+    mfma_begin(0);
     prio_hi();
     qk_step<DT, QB>(k_addr(0), la, qf, s);
     prio_lo();
+    mfma_end();
     barrier();
+    softmax_begin(0);
     softmax_keep_o(0);
-    landed();
+    softmax_end();
     barrier();
     for (j = 1; j < n_wave; ++j) {
-      loads(j);
+      mfma_begin(j);
       prio_hi();
       pv_step<DT, QB>(v_addr(j - 1), la, pf, acc);
       qk_step<DT, QB>(k_addr(j), la, qf, s);
       prio_lo();
+      mfma_end();
       barrier();
+      softmax_begin(j);
       const bool moved = softmax_keep_o(j);
-      landed();
+      softmax_end();
       barrier();
       if (moved) {
 #pragma unroll
@@ -212,29 +236,35 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fa_fwd_kernel(
       }
     }
     for (; j < n_wave; ++j) {
-      loads(j);
+      mfma_begin(j);
       prio_hi();
       pv_step<DT, QB>(v_addr(j - 1), la, pf, acc);
       qk_step<DT, QB>(k_addr(j), la, qf, s);
       prio_lo();
+      mfma_end();
       barrier();
+      softmax_begin(j);
       softmax_scale_o(j);
-      landed();
+      softmax_end();
       barrier();
     }
-    loads(j);
+    mfma_begin(j);
     prio_hi();
     pv_step<DT, QB>(v_addr(j - 1), la, pf, acc);
     prio_lo();
+    mfma_end();
     barrier();
-    landed();
+    softmax_begin(j);
+    softmax_end();
     barrier();
     ++j;
   }
   for (; j <= n_tiles; ++j) {  // steps with nothing left for this wave
-    loads(j);
+    mfma_begin(j);
+    mfma_end();
     barrier();
-    landed();
+    softmax_begin(j);
+    softmax_end();
     barrier();
   }
   if (group_a) barrier();
