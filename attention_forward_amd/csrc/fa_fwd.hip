@@ -95,10 +95,11 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fa_fwd_kernel(
 #pragma unroll
   for (int db = 0; db < 4; ++db) acc[db][0] = f32x16{};
 
-  // One group (4 waves) loads every tile: chunk 4c + w (w = wave & 3) covers
-  // rows 16c + 4w + lane/16, one swizzle pattern (and so one lane offset) per
-  // wave for every chunk
-  constexpr int LOADERS = NW / 2;
+  // The loading waves split every tile: with L of them, chunk L*c + w covers
+  // rows 4(L*c + w) + lane/16 (w = the wave's index among the loaders); L*c*4
+  // is a multiple of 16 rows, so one swizzle pattern (and one lane offset)
+  // serves all of a wave's chunks
+  constexpr int LOADERS = ATTN_LOADERS == 2 ? NW : NW / 2;
   constexpr int CHUNKS_PER_LOADER = (KT / 4) / LOADERS;
   const unsigned koff = load_lane_offset<false>(wave & (LOADERS - 1));
   const unsigned voff = load_lane_offset<true>(wave & (LOADERS - 1));
@@ -130,20 +131,22 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fa_fwd_kernel(
   // of step j+1.
   // The loads of step j, K(j+1) and V(j), are issued at the start of the
   // half-step in which A runs its MFMA phase j, and have landed by the end of
-  // the next one.  ATTN_LOADER_B selects which group does it: A, at the start
-  // of its MFMA phase and waiting at the end of its softmax phase, or B, at
-  // the start of its softmax phase (of step j-1) and waiting at the end of its
-  // MFMA phase j.  Either way the stages written are free (last read before
-  // the barrier that opens the half-step) and are next read after the barrier
-  // that closes the wait.
-  constexpr bool B_LOADS = ATTN_LOADER_B != 0;
-  const bool loader = B_LOADS ? !group_a : group_a;
+  // the next one.  A issues its share at the start of its MFMA phase and waits
+  // at the end of its softmax phase; B issues its share at the start of its
+  // softmax phase (of step j-1) and waits at the end of its MFMA phase j.
+  // Either way the stages written are free (last read before the barrier that
+  // opens the half-step) and are next read after the barrier that closes the
+  // wait.  ATTN_LOADERS: 0 = A loads everything, 1 = B does, 2 = both halves
+  // (the issue of direct-to-LDS loads holds up the issuing wave for a while,
+  // so the cost is best split between the two phases of the half-step).
+  constexpr bool A_LOADS = ATTN_LOADERS != 1, B_LOADS = ATTN_LOADERS != 0;
+  const bool loader = group_a ? A_LOADS : B_LOADS;
   auto issue_step = [&](int j) {
     if (j + 1 < n_tiles) issue(kh, koff, j + 1, k_stage(j + 1));
     if (j < n_tiles) issue(vh, voff, j, v_stage(j));
   };
   auto mfma_begin = [&](int j) {
-    if (!B_LOADS && group_a) issue_step(j);
+    if (A_LOADS && group_a) issue_step(j);
   };
   auto mfma_end = [&]() {
     if (B_LOADS && !group_a) vm_wait_all();
@@ -152,7 +155,7 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fa_fwd_kernel(
     if (B_LOADS && !group_a) issue_step(j + 1);
   };
   auto softmax_end = [&]() {
-    if (!B_LOADS && group_a) vm_wait_all();
+    if (A_LOADS && group_a) vm_wait_all();
   };
   auto barrier = [] { __builtin_amdgcn_s_barrier(); };
   auto k_addr = [&](int j) { return lds_base + (unsigned)((j & 1) * TILE_BYTES); };

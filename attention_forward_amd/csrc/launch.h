@@ -47,9 +47,10 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_decode_split(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 
-// Which wave group of the prefill kernel issues the K/V tile loads (0: A, 1: B).
-#ifndef ATTN_LOADER_B
-#define ATTN_LOADER_B 1
+// Which wave groups of the prefill kernel issue the K/V tile loads
+// (0: group A, 1: group B, 2: both, half each).
+#ifndef ATTN_LOADERS
+#define ATTN_LOADERS 1
 #endif
 
 // Number of 32-query blocks per wave and waves per workgroup of the prefill kernel.
