@@ -18,7 +18,7 @@ beside it.  The oracle's
 sample also checks the GPU output on those rows; a failing check prints no
 throughput.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5]
+    python bench.py [--gpus 1] [--steps 100] [--warmup 30]
 """
 from __future__ import annotations
 
@@ -165,6 +165,25 @@ def ratio(a, b):
     return None if b is None or not math.isfinite(b) else round(a / b, 4)
 
 
+def gpu_state():
+    """Clocks, power and temperature of GPU 0 as rocm-smi reports them (None
+    where the tool is missing or fails); taken before and after the timed steps."""
+    import subprocess
+
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--showtemp", "--json"],
+                           capture_output=True, text=True, timeout=30)
+        data = json.loads(r.stdout)
+    except Exception:  # no tool, no permission, or not JSON: report nothing
+        return None
+    card = data.get("card0") if isinstance(data, dict) else None
+    if not isinstance(card, dict):
+        return None
+    keep = ("sclk", "mclk", "fclk", "socclk", "power", "temperature", "junction", "edge",
+            "memory")
+    return {k: v for k, v in card.items() if any(w in k.lower() for w in keep)}
+
+
 def spread(xs):
     """median, p10 and p90 of a list of durations (ms)."""
     t = sorted(xs)
@@ -243,8 +262,9 @@ def decode_parity(q, k, v, o_gpu, n_rows=64):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=30,
+                    help="untimed steps first: the clock settles over the first dozen or so")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target wall time of the oracle's CPU-baseline sample")
     ap.add_argument("--skip-cpu-baseline", action="store_true",
@@ -293,6 +313,7 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    state_before = None if args.skip_context else gpu_state()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -300,6 +321,7 @@ def main():
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    state_after = None if args.skip_context else gpu_state()
     pre_ms = [e[0].elapsed_time(e[1]) for e in evs]
     dec_ms = [e[1].elapsed_time(e[2]) for e in evs]
     pre_avg = sum(pre_ms) / len(pre_ms)
@@ -366,6 +388,7 @@ def main():
                                     "unit": "GB/s",
                                     "shape": stream_shape, "bytes": 4 << 30},
         "other_workloads": others,
+        "gpu_state": {"before": state_before, "after": state_after},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_MFMA_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_MFMA_TFLOPS, 4),
                      "traffic": None if traffic_pre is None else traffic_pre["bytes"],
