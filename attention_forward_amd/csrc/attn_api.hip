@@ -65,7 +65,8 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
     return fail(ATTN_ERR_SHAPE, "attn_fwd: Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
   if (dtype != ATTN_F16 && dtype != ATTN_BF16)
     return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd: dtype %d is not 0 (fp16) or 1 (bf16)", dtype);
-  if (d != attn::HEAD_DIM) return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd: head dim %d (only 128)", d);
+  if (!attn::head_dim_supported(d))
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd: head dim %d (64 and 128 are implemented)", d);
   if (causal != 0 && causal != 1) return fail(ATTN_ERR_VALUE, "attn_fwd: causal must be 0 or 1");
   if (!std::isfinite(scale) || scale < 0.0f)
     return fail(ATTN_ERR_VALUE, "attn_fwd: scale must be finite and >= 0");
@@ -81,7 +82,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
     return fail(ATTN_ERR_SHAPE, "attn_fwd: sequence length above %d", kMaxSeq);
   int st = check_device();
   if (st != ATTN_OK) return st;
-  attn::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, causal, fold_log2e(scale), dtype};
+  attn::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, d, causal, fold_log2e(scale), dtype};
   return hip_status(attn::launch_fwd(a, static_cast<hipStream_t>(stream)), "attn_fwd launch");
 }
 
@@ -101,15 +102,16 @@ int attn_splitkv_combine(const float* o_part, const float* lse_part, void* o, fl
   if (num_splits <= 0) return fail(ATTN_ERR_VALUE, "attn_splitkv_combine: num_splits must be >= 1");
   if (dtype != ATTN_F16 && dtype != ATTN_BF16)
     return fail(ATTN_ERR_UNSUPPORTED, "attn_splitkv_combine: dtype %d", dtype);
-  if (d != attn::HEAD_DIM)
-    return fail(ATTN_ERR_UNSUPPORTED, "attn_splitkv_combine: head dim %d (only 128)", d);
+  if (!attn::head_dim_supported(d))
+    return fail(ATTN_ERR_UNSUPPORTED,
+                "attn_splitkv_combine: head dim %d (64 and 128 are implemented)", d);
   if (!aligned16(o_part) || !aligned4(lse_part) || !aligned16(o) || (lse && !aligned4(lse)))
     return fail(ATTN_ERR_ALIGN, "attn_splitkv_combine: misaligned pointer");
   if ((long long)B * Hq > INT_MAX)
     return fail(ATTN_ERR_SHAPE, "attn_splitkv_combine: too many rows");
   int st = check_device();
   if (st != ATTN_OK) return st;
-  attn::CombineArgs a{o_part, lse_part, o, lse, B * Hq, num_splits, dtype};
+  attn::CombineArgs a{o_part, lse_part, o, lse, B * Hq, num_splits, d, dtype};
   return hip_status(attn::launch_combine(a, static_cast<hipStream_t>(stream)),
                     "attn_splitkv_combine launch");
 }
@@ -126,7 +128,9 @@ int attn_fwd_decode(const void* q, const void* k, const void* v, void* o, float*
     return fail(ATTN_ERR_SHAPE, "attn_fwd_decode: Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
   if (dtype != ATTN_F16 && dtype != ATTN_BF16)
     return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd_decode: dtype %d", dtype);
-  if (d != attn::HEAD_DIM) return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd_decode: head dim %d (only 128)", d);
+  if (!attn::head_dim_supported(d))
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd_decode: head dim %d (64 and 128 are implemented)",
+                d);
   if (Hq / Hkv > 32)
     return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd_decode: query heads per kv head %d > 32",
                 Hq / Hkv);
@@ -153,11 +157,11 @@ int attn_fwd_decode(const void* q, const void* k, const void* v, void* o, float*
   float* lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                              round_up(rows * d * sizeof(float)));
   hipStream_t s = static_cast<hipStream_t>(stream);
-  attn::DecodeArgs da{q, k, v, o_part, lse_part, B, Hq, Hkv, Sk, num_splits, fold_log2e(scale),
-                      dtype};
+  attn::DecodeArgs da{q, k, v, o_part, lse_part, B, Hq, Hkv, Sk, d, num_splits,
+                      fold_log2e(scale), dtype};
   st = hip_status(attn::launch_decode_split(da, s), "attn_fwd_decode split launch");
   if (st != ATTN_OK) return st;
-  attn::CombineArgs ca{o_part, lse_part, o, lse, B * Hq, num_splits, dtype};
+  attn::CombineArgs ca{o_part, lse_part, o, lse, B * Hq, num_splits, d, dtype};
   return hip_status(attn::launch_combine(ca, s), "attn_fwd_decode combine launch");
 }
 

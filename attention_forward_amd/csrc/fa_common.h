@@ -22,10 +22,24 @@
 
 namespace attn {
 
-constexpr int D = 128;          // head dimension handled by these kernels (HEAD_DIM)
-constexpr int KT = 64;          // keys per K/V tile
-constexpr int ROW = D * 2;      // bytes per K/V row in LDS (16-bit elements)
-constexpr int TILE_BYTES = KT * ROW;  // 16 KiB per K or V tile
+constexpr int KT = 64;  // keys per K/V tile
+
+// Geometry of one head dimension HD (64 or 128): a K or V row is HD 16-bit
+// elements, read in 16-byte slots; a direct-to-LDS load instruction moves a
+// 1 KiB chunk of whole rows.
+template <int HD>
+struct Geom {
+  static_assert(HD == 64 || HD == 128, "head dimensions 64 and 128");
+  static constexpr int ROW = HD * 2;            // bytes per row
+  static constexpr int SLOTS = ROW / 16;        // 16-byte slots per row
+  static constexpr int TILE = KT * ROW;         // bytes per K or V tile
+  static constexpr int RPC = 1024 / ROW;        // rows per 1 KiB load chunk
+  static constexpr int CHUNKS = TILE / 1024;    // load chunks per tile
+  static constexpr int DSTEPS = HD / 16;        // 16-deep d-steps of S^T = K Q^T
+  static constexpr int DBLOCKS = HD / 32;       // 32-wide d-blocks of O^T
+  static constexpr int KOPS = 2 * DSTEPS;       // K operands per tile (2 key blocks)
+  static constexpr int VOPS = 4 * DBLOCKS;      // V^T operands per tile (4 key steps)
+};
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -91,34 +105,52 @@ __device__ __forceinline__ float half_sum(float x) {
   return __builtin_bit_cast(float, (int)r[0]) + __builtin_bit_cast(float, (int)r[1]);
 }
 
-// ---- LDS swizzles (16-byte slots, 16 slots per 256-byte row) ----
-// K is read 16 bytes per lane, 32 consecutive rows at one slot: XOR the slot
-// with the low 4 row bits so 8 or 16 consecutive rows hit distinct banks.
-__device__ __forceinline__ int k_swz(int row) { return row & 15; }
+// ---- LDS swizzles (16-byte slots) ----
+// The 64 banks of 4 bytes span 256 bytes: one row at HD = 128, two rows at
+// HD = 64.
+// K is read 16 bytes per lane, 32 consecutive rows at one slot.  HD = 128:
+// XOR the slot with the low 4 row bits so 16 consecutive rows hit distinct
+// banks.  HD = 64: rows of equal parity share a bank half, so XOR with row
+// bits 1-3, which differ across the 8 rows of each parity among 16.
+template <int HD>
+__device__ __forceinline__ int k_swz(int row) {
+  if constexpr (HD == 128)
+    return row & 15;
+  else
+    return (row >> 1) & 7;
+}
 // V is read with the 8-byte transposing read: each 16-lane group covers 4
-// consecutive rows x 32 bytes.  XOR with f(row & 3) = 2a ^ 8(a & 1) spreads those
-// rows over distinct 32-byte bank groups (bits 1-2) and distinct 64-byte groups
-// (bits 2-3).
+// consecutive rows x 32 bytes, and two groups the same rows at the next 32
+// bytes.  HD = 128: XOR with f(row & 3) = 2a ^ 8(a & 1) spreads those rows
+// over distinct 32-byte bank groups (bits 1-2) and distinct 64-byte groups
+// (bits 2-3).  HD = 64: rows r and r + 2 share a bank half; XOR with 4 for
+// row bit 1 moves one of them to the other 64 bytes of that half.
+template <int HD>
 __device__ __forceinline__ int v_swz(int row) {
-  int a = row & 3;
-  return (a << 1) ^ ((a & 1) << 3);
+  if constexpr (HD == 128) {
+    int a = row & 3;
+    return (a << 1) ^ ((a & 1) << 3);
+  } else {
+    return ((row >> 1) & 1) << 2;
+  }
 }
 
 // ---- HBM -> LDS tile load ----
 // One wave instruction of a direct-to-LDS load moves 64 x 16 B into 1 KiB of
-// LDS at base + 16*lane, i.e. 4 full rows.  The lane that fills LDS slot p of
-// row r reads global slot p ^ swz(r) of that row, so LDS slot s ^ swz(r) holds
-// the row's logical slot s.
+// LDS at base + 16*lane, i.e. RPC full rows.  The lane that fills LDS slot p
+// of row r reads global slot p ^ swz(r) of that row, so LDS slot s ^ swz(r)
+// holds the row's logical slot s.
 // Per-lane byte offset, within a 1 KiB load chunk, of the 16-byte source slot
-// the lane fetches: row (chunk*4 + lane/16), slot (lane%16) ^ swz(row).  With
-// chunks stepping by 4 rows per wave and 16 rows per round, the row bits the
-// swizzles use are fixed per lane, so one offset serves a whole tile.
-template <bool IS_V>
+// the lane fetches: row (chunk*RPC + lane/SLOTS), slot (lane%SLOTS) ^ swz(row).
+// A chunk index that advances by a multiple of 16 rows keeps the row bits the
+// swizzles use, so one offset serves all of a lane's chunks that far apart.
+template <int HD, bool IS_V>
 __device__ __forceinline__ unsigned load_lane_offset(int chunk) {
+  using G = Geom<HD>;
   const int lane = threadIdx.x & 63;
-  const int r = chunk * 4 + (lane >> 4);
-  const int slot = (lane & 15) ^ (IS_V ? v_swz(r) : k_swz(r));
-  return (unsigned)(r * ROW + slot * 16);
+  const int r = chunk * G::RPC + lane / G::SLOTS;
+  const int slot = (lane % G::SLOTS) ^ (IS_V ? v_swz<HD>(r) : k_swz<HD>(r));
+  return (unsigned)(r * G::ROW + slot * 16);
 }
 
 // ---- bounds-checked buffer loads ----
@@ -176,57 +208,64 @@ __device__ __forceinline__ void lgkm_wait(u32x4& x) {
 }
 
 // Per-lane LDS byte addresses (relative to a K/V stage) that stay fixed for
-// the whole key loop; tile, stage and step offsets are immediates.
+// the whole key loop; tile, stage and step offsets are immediates.  Entries
+// past the head dimension's d-steps and d-blocks are unused.
 struct LaneAddr {
   unsigned k[8];  // K operand of d-step st (key block 0; block 1 is +32 rows)
   unsigned v[4];  // V^T operand of d-block db (key step 0; others are row offsets)
 };
 
+template <int HD>
 __device__ __forceinline__ LaneAddr lane_addresses() {
+  using G = Geom<HD>;
   const int lane = threadIdx.x & 63;
   const int g = lane >> 5, n = lane & 31, j = lane & 15, h = (lane >> 4) & 1;
-  LaneAddr a;
+  LaneAddr a = {};
 #pragma unroll
-  for (int st = 0; st < 8; ++st)
-    a.k[st] = (unsigned)(n * ROW + (((2 * st + g) ^ k_swz(n)) * 16));
+  for (int st = 0; st < G::DSTEPS; ++st)
+    a.k[st] = (unsigned)(n * G::ROW + (((2 * st + g) ^ k_swz<HD>(n)) * 16));
   // V^T reads: rows 4g + (j>>2) (+16t, +32kb, +8 for items 4..7), 32-byte column
   // group 4db + 2h, 8-byte half (j&3)>>1 ... see v_swz
   const int row_l = 4 * g + (j >> 2);
 #pragma unroll
-  for (int db = 0; db < 4; ++db) {
+  for (int db = 0; db < G::DBLOCKS; ++db) {
     const int slot = 4 * db + 2 * h + ((j & 3) >> 1);
-    a.v[db] = (unsigned)(row_l * ROW + ((slot ^ v_swz(row_l)) * 16) + 8 * (j & 1));
+    a.v[db] = (unsigned)(row_l * G::ROW + ((slot ^ v_swz<HD>(row_l)) * 16) + 8 * (j & 1));
   }
   return a;
 }
 
 // ---- the three parts of one 64-key tile, for QB blocks of 32 queries ----
 //
-// qf: Q^T operands [QB][8] (16-deep d steps).  s: S^T accumulators [2 key
-// blocks][QB].  o: O^T accumulators [4 d-blocks][QB].  m: reference max (log2
-// units, -inf initially); l: this lane's running sum over its half of the keys.
-// key0: global index of the tile's first key; qrow0: global index of the
-// wave's first query.  Online softmax across tiles: "The FA5090 Optimization
-// Journey", sec. 2.6 (exp2 with log2 e folded into the scale, running max in
-// the log2 domain) and sec. 2.8 (effective max of a fully masked tile); "10
-// rounds of hand-written fused attention ...", round R8 (m and l carried).
+// qf: Q^T operands [QB][DSTEPS] (16-deep d steps).  s: S^T accumulators [2 key
+// blocks][QB].  o: O^T accumulators [DBLOCKS d-blocks][QB].  m: reference max
+// (log2 units, -inf initially); l: this lane's running sum over its half of
+// the keys.  key0: global index of the tile's first key; qrow0: global index
+// of the wave's first query.  Online softmax across tiles: "The FA5090
+// Optimization Journey", sec. 2.6 (exp2 with log2 e folded into the scale,
+// running max in the log2 domain) and sec. 2.8 (effective max of a fully
+// masked tile); "10 rounds of hand-written fused attention ...", round R8 (m
+// and l carried).
 
-// S^T = K Q^T: 2 key blocks x 8 d-steps; K operands read KD steps ahead.
+// S^T = K Q^T: 2 key blocks x DSTEPS d-steps; K operands read KD steps ahead.
 // kbase: LDS address of the K tile.
-template <int DT, int QB>
+template <int DT, int QB, int HD>
 __device__ __forceinline__ void qk_step(unsigned kbase, const LaneAddr& la,
-                                        const u32x4 (&qf)[QB][8], f32x16 (&s)[2][QB]) {
+                                        const u32x4 (&qf)[QB][Geom<HD>::DSTEPS],
+                                        f32x16 (&s)[2][QB]) {
+  using G = Geom<HD>;
+  constexpr int DS = G::DSTEPS, N = G::KOPS;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) s[kb][qb] = f32x16{};
-  constexpr int KD = ATTN_KDEPTH;
+  constexpr int KD = ATTN_KDEPTH < N ? ATTN_KDEPTH : N;
   u32x4 ko[KD];
   auto read_k = [&](int i, u32x4& dst) {
-    // i = kb * 8 + st
+    // i = kb * DS + st (cases past N are never taken)
 #define ATTN_KREAD(I)                                                                  \
   case I:                                                                              \
-    dst = lds_b128<((I) >> 3) * 32 * ROW>(kbase + la.k[(I) & 7]);                     \
+    dst = lds_b128<((I) / DS) * 32 * G::ROW>(kbase + la.k[(I) % DS]);                 \
     break;
     switch (i) {
       ATTN_KREAD(0) ATTN_KREAD(1) ATTN_KREAD(2) ATTN_KREAD(3) ATTN_KREAD(4) ATTN_KREAD(5)
@@ -238,11 +277,11 @@ __device__ __forceinline__ void qk_step(unsigned kbase, const LaneAddr& la,
 #pragma unroll
   for (int i = 0; i < KD; ++i) read_k(i, ko[i]);
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
+  for (int i = 0; i < N; ++i) {
     u32x4& cur = ko[i % KD];
-    // reads issued so far: min(16, KD + i); read i is done when at most
+    // reads issued so far: min(N, KD + i); read i is done when at most
     // (issued - i - 1) younger ones are outstanding
-    switch (i + KD < 16 ? KD - 1 : 15 - i) {
+    switch (i + KD < N ? KD - 1 : N - 1 - i) {
       case 7: lgkm_wait<7>(cur); break;
       case 6: lgkm_wait<6>(cur); break;
       case 5: lgkm_wait<5>(cur); break;
@@ -252,10 +291,10 @@ __device__ __forceinline__ void qk_step(unsigned kbase, const LaneAddr& la,
       case 1: lgkm_wait<1>(cur); break;
       default: lgkm_wait<0>(cur); break;
     }
-    const int kb = i >> 3, st = i & 7;
+    const int kb = i / DS, st = i % DS;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) s[kb][qb] = mfma<DT>(cur, qf[qb][st], s[kb][qb]);
-    if (i + KD < 16) read_k(i + KD, ko[i % KD]);
+    if (i + KD < N) read_k(i + KD, ko[i % KD]);
   }
 }
 
@@ -277,8 +316,8 @@ __device__ __forceinline__ void qk_step(unsigned kbase, const LaneAddr& la,
 // which O must be multiplied by alpha: a row whose max was -inf has O = 0).
 // The caller then applies alpha itself; until that happens alpha is exactly 1
 // for every lane, so skipping the multiply changes no bit.
-template <int DT, int QB, bool MASK, bool RESCALE_O = true>
-__device__ __forceinline__ bool softmax_step(f32x16 (&s)[2][QB], f32x16 (&o)[4][QB],
+template <int DT, int QB, bool MASK, bool RESCALE_O = true, int NDB = 4>
+__device__ __forceinline__ bool softmax_step(f32x16 (&s)[2][QB], f32x16 (&o)[NDB][QB],
                                              float (&m)[QB], float (&l)[QB],
                                              u32x4 (&pf)[2][2][QB], float scale_log2, int key0,
                                              int qrow0, int n_keys, bool causal, int causal_off,
@@ -322,7 +361,7 @@ __device__ __forceinline__ bool softmax_step(f32x16 (&s)[2][QB], f32x16 (&o)[4][
     alpha_out[qb] = alpha;
     if constexpr (RESCALE_O) {
 #pragma unroll
-      for (int db = 0; db < 4; ++db) o[db][qb] *= alpha;
+      for (int db = 0; db < NDB; ++db) o[db][qb] *= alpha;
     }
     // effective max of a row that has seen no visible key yet ("The FA5090
     // Optimization Journey", sec. 2.8): exp2(-inf - 0) = 0 keeps it NaN-free
@@ -358,20 +397,25 @@ __device__ __forceinline__ bool softmax_step(f32x16 (&s)[2][QB], f32x16 (&o)[4][
     return __builtin_amdgcn_ballot_w64(moved) != 0;
 }
 
-// O^T += V^T P^T: 4 d-blocks x 4 key steps, operands 4 steps ahead.  Step i:
-// db = i >> 2, kb = (i >> 1) & 1, t = i & 1; the operand's two transposing
-// reads cover keys 32kb + 16t + 4g + {0..3} and the same + 8.  vbase: LDS
-// address of the V tile.
-template <int DT, int QB>
+// O^T += V^T P^T: DBLOCKS d-blocks x 4 key steps, operands 4 steps ahead.
+// Step i: db = i >> 2, kb = (i >> 1) & 1, t = i & 1; the operand's two
+// transposing reads cover keys 32kb + 16t + 4g + {0..3} and the same + 8.
+// vbase: LDS address of the V tile.
+template <int DT, int QB, int HD>
 __device__ __forceinline__ void pv_step(unsigned vbase, const LaneAddr& la,
-                                        const u32x4 (&pf)[2][2][QB], f32x16 (&o)[4][QB]) {
+                                        const u32x4 (&pf)[2][2][QB],
+                                        f32x16 (&o)[Geom<HD>::DBLOCKS][QB]) {
+  using G = Geom<HD>;
+  constexpr int N = G::VOPS;
   u32x4 vo[4];
   auto read_v = [&](int i, u32x4& dst) {
     u32x2 lo, hi;
+    // cases past N are never taken
 #define ATTN_VREAD(I)                                                                  \
   case I:                                                                              \
-    lo = lds_tr16<(32 * (((I) >> 1) & 1) + 16 * ((I) & 1)) * ROW>(vbase + la.v[(I) >> 2]); \
-    hi = lds_tr16<(32 * (((I) >> 1) & 1) + 16 * ((I) & 1) + 8) * ROW>(                 \
+    lo = lds_tr16<(32 * (((I) >> 1) & 1) + 16 * ((I) & 1)) * G::ROW>(                  \
+        vbase + la.v[(I) >> 2]);                                                       \
+    hi = lds_tr16<(32 * (((I) >> 1) & 1) + 16 * ((I) & 1) + 8) * G::ROW>(              \
         vbase + la.v[(I) >> 2]);                                                       \
     break;
     switch (i) {
@@ -385,10 +429,10 @@ __device__ __forceinline__ void pv_step(unsigned vbase, const LaneAddr& la,
 #pragma unroll
   for (int i = 0; i < 4; ++i) read_v(i, vo[i]);
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
+  for (int i = 0; i < N; ++i) {
     u32x4& cur = vo[i & 3];
-    // two reads per operand; operands issued so far: min(16, 4 + i)
-    switch (i + 4 < 16 ? 6 : 2 * (15 - i)) {
+    // two reads per operand; operands issued so far: min(N, 4 + i)
+    switch (i + 4 < N ? 6 : 2 * (N - 1 - i)) {
       case 6: lgkm_wait<6>(cur); break;
       case 4: lgkm_wait<4>(cur); break;
       case 2: lgkm_wait<2>(cur); break;
@@ -397,24 +441,8 @@ __device__ __forceinline__ void pv_step(unsigned vbase, const LaneAddr& la,
     const int db = i >> 2, kb = (i >> 1) & 1, t = i & 1;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) o[db][qb] = mfma<DT>(cur, pf[kb][t][qb], o[db][qb]);
-    if (i + 4 < 16) read_v(i + 4, vo[i & 3]);
+    if (i + 4 < N) read_v(i + 4, vo[i & 3]);
   }
-}
-
-// The whole tile in one wave: S^T, softmax, O^T.
-template <int DT, int QB, bool MASK>
-__device__ __forceinline__ void tile_step(unsigned kbase, unsigned vbase, const LaneAddr& la,
-                                          const u32x4 (&qf)[QB][8], f32x16 (&o)[4][QB],
-                                          float (&m)[QB], float (&l)[QB], float scale_log2,
-                                          int key0, int qrow0, int n_keys, bool causal,
-                                          int causal_off) {
-  f32x16 s[2][QB];
-  u32x4 pf[2][2][QB];
-  qk_step<DT, QB>(kbase, la, qf, s);
-  float alpha[QB];
-  softmax_step<DT, QB, MASK>(s, o, m, l, pf, scale_log2, key0, qrow0, n_keys, causal,
-                             causal_off, alpha);
-  pv_step<DT, QB>(vbase, la, pf, o);
 }
 
 }  // namespace attn

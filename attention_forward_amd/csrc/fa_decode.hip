@@ -27,11 +27,13 @@ namespace attn {
 // requested at launch rather than declared because a static 64 KiB array
 // makes the compiler assume one wave per SIMD and move the accumulator into
 // AGPRs.
-template <int DT>
+template <int DT, int HD>
 __global__ __launch_bounds__(64, 2) void fa_decode_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, float* __restrict__ o_part, float* __restrict__ lse_part,
     int Hq, int Hkv, int Sk, int num_splits, float scale_log2) {
+  using Gm = Geom<HD>;
+  constexpr int D = HD, ROW = Gm::ROW, TILE_BYTES = Gm::TILE;
   extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];  // >= 2 tiles
   const int lane = threadIdx.x & 63;
   const int g = lane >> 5;
@@ -52,7 +54,7 @@ __global__ __launch_bounds__(64, 2) void fa_decode_split_kernel(
   const uint16_t* vh = v + (size_t)bk * Sk * D;
 
   // the group's query heads fill slots 0..G-1; slots past G read as zeros
-  u32x4 qf[1][8];
+  u32x4 qf[1][Gm::DSTEPS];
   const bool slot_used = n < G;
   const size_t qrow = (size_t)b * Hq + (size_t)hkv * G + n;  // Sq == 1
   {
@@ -60,41 +62,43 @@ __global__ __launch_bounds__(64, 2) void fa_decode_split_kernel(
         make_rsrc(q + ((size_t)b * Hq + (size_t)hkv * G) * D, (long long)G * ROW);
     const unsigned row_off = (unsigned)(n * ROW + 16 * g);
 #pragma unroll
-    for (int st = 0; st < 8; ++st) qf[0][st] = load_b128(qr, row_off + 32 * st);
+    for (int st = 0; st < Gm::DSTEPS; ++st) qf[0][st] = load_b128(qr, row_off + 32 * st);
   }
 
-  f32x16 acc[4][1];
+  f32x16 acc[Gm::DBLOCKS][1];
   float m[1] = {-INFINITY}, l[1] = {0.0f};
 #pragma unroll
-  for (int db = 0; db < 4; ++db) acc[db][0] = f32x16{};
+  for (int db = 0; db < Gm::DBLOCKS; ++db) acc[db][0] = f32x16{};
 
   unsigned char ATTN_LDS* kt = (unsigned char ATTN_LDS*)(smem);
   unsigned char ATTN_LDS* vt = kt + TILE_BYTES;
-  const LaneAddr la = lane_addresses();
+  const LaneAddr la = lane_addresses<HD>();
   const unsigned base = (unsigned)(size_t)kt;
-  // chunk c covers rows 4c + lane/16: the K swizzle repeats every 4 chunks,
-  // the V swizzle is the same for every chunk
-  unsigned koff[4];
+  // chunk c covers rows RPC*c + lane/SLOTS: the K swizzle repeats every 16
+  // rows (KP chunks), the V swizzle is the same for every chunk
+  constexpr int KP = 16 / Gm::RPC;
+  unsigned koff[KP];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) koff[c] = load_lane_offset<false>(c);
-  const unsigned voff = load_lane_offset<true>(0);
+  for (int c = 0; c < KP; ++c) koff[c] = load_lane_offset<HD, false>(c);
+  const unsigned voff = load_lane_offset<HD, true>(0);
   // K and V stages refill independently: K(t+1) is issued as soon as QK(t)
   // has read the K stage and V(t+1) as soon as PV(t) has read the V stage, so
   // the next tile's bytes are in flight while this tile is computed.  Loads
   // complete in issue order (K(t), V(t), K(t+1), V(t+1), ...), so "K(t) has
   // landed" is vmcnt <= one tile half (V(t)) and "V(t) has landed" is
   // vmcnt <= one tile half (K(t+1)) or 0 on the last tile.
-  constexpr int HALF = KT / 4;  // load instructions per K or V tile
+  constexpr int HALF = Gm::CHUNKS;  // load instructions per K or V tile
   auto issue_k = [&](int key0) {
     // keys past the split read as zeros
     const __amdgpu_buffer_rsrc_t r = make_rsrc(kh + (size_t)key0 * D, (long long)(j1 - key0) * ROW);
 #pragma unroll
-    for (int c = 0; c < HALF; ++c) load_chunk(r, koff[c & 3] + (c >> 2) * 16 * ROW, kt + c * 1024);
+    for (int c = 0; c < HALF; ++c)
+      load_chunk(r, koff[c % KP] + (c / KP) * 16 * ROW, kt + c * 1024);
   };
   auto issue_v = [&](int key0) {
     const __amdgpu_buffer_rsrc_t r = make_rsrc(vh + (size_t)key0 * D, (long long)(j1 - key0) * ROW);
 #pragma unroll
-    for (int c = 0; c < HALF; ++c) load_chunk(r, voff + c * 4 * ROW, vt + c * 1024);
+    for (int c = 0; c < HALF; ++c) load_chunk(r, voff + c * 1024, vt + c * 1024);
   };
   // every LDS read issued so far has returned (the stage may be overwritten)
   auto lds_drained = [] { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); };
@@ -104,18 +108,24 @@ __global__ __launch_bounds__(64, 2) void fa_decode_split_kernel(
     // Q has landed; K(0) and V(0) may still be in flight.  Tying Q's registers
     // to the wait keeps it after the tile loads and tells the compiler that Q is
     // ready, so it does not wait for every load before the loop.
-    asm volatile("s_waitcnt vmcnt(%8)"
-                 : "+v"(qf[0][0]), "+v"(qf[0][1]), "+v"(qf[0][2]), "+v"(qf[0][3]),
-                   "+v"(qf[0][4]), "+v"(qf[0][5]), "+v"(qf[0][6]), "+v"(qf[0][7])
-                 : "n"(2 * HALF)
-                 : "memory");
+    if constexpr (Gm::DSTEPS == 8)
+      asm volatile("s_waitcnt vmcnt(%8)"
+                   : "+v"(qf[0][0]), "+v"(qf[0][1]), "+v"(qf[0][2]), "+v"(qf[0][3]),
+                     "+v"(qf[0][4]), "+v"(qf[0][5]), "+v"(qf[0][6]), "+v"(qf[0][7])
+                   : "n"(2 * HALF)
+                   : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(%4)"
+                   : "+v"(qf[0][0]), "+v"(qf[0][1]), "+v"(qf[0][2]), "+v"(qf[0][3])
+                   : "n"(2 * HALF)
+                   : "memory");
   }
   for (int key0 = j0; key0 < j1; key0 += KT) {
     const bool more = key0 + KT < j1;
     f32x16 s[2][1];
     u32x4 pf[2][2][1];
     vm_wait<HALF>();  // K(t)
-    qk_step<DT, 1>(base, la, qf, s);
+    qk_step<DT, 1, HD>(base, la, qf, s);
     lds_drained();
     if (more) issue_k(key0 + KT);
     float alpha[1];
@@ -127,7 +137,7 @@ __global__ __launch_bounds__(64, 2) void fa_decode_split_kernel(
       vm_wait<HALF>();  // V(t); K(t+1) may be in flight
     else
       vm_wait_all();
-    pv_step<DT, 1>(base + TILE_BYTES, la, pf, acc);
+    pv_step<DT, 1, HD>(base + TILE_BYTES, la, pf, acc);
     lds_drained();
     if (more) issue_v(key0 + KT);
   }
@@ -138,7 +148,7 @@ __global__ __launch_bounds__(64, 2) void fa_decode_split_kernel(
     const size_t prow = qrow * num_splits + split;
     float* op = o_part + prow * D;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+    for (int db = 0; db < Gm::DBLOCKS; ++db)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int d0 = 32 * db + 8 * jj + 4 * g;
@@ -153,24 +163,34 @@ __global__ __launch_bounds__(64, 2) void fa_decode_split_kernel(
 }
 
 // One wave per (batch, query head) row, COMBINE_ROWS rows per workgroup; lane
-// c owns columns 2c and 2c+1.  Splits are merged COMBINE_BLOCK at a time with
+// c owns columns HD/64 * c onwards (two at HD = 128, one at HD = 64).  Splits
+// are merged COMBINE_BLOCK at a time with
 // the online-softmax rescale (running max M, running sum L): a block's partial
 // LSEs (wave-uniform, scalar loads) and partial outputs are loaded together, so
 // a row costs one memory round trip per block rather than a max pass followed
 // by a weighted-sum pass.
 constexpr int COMBINE_ROWS = 4;
 constexpr int COMBINE_BLOCK = 16;
-static_assert(D == 128, "a wave covers one row of 128 columns, two per lane");
 
-template <int DT>
+// partial outputs of one split for this lane's columns (HD / 64 of them)
+template <int HD>
+__device__ __forceinline__ float2 load_cols(const float* p) {
+  if constexpr (HD == 128)
+    return *reinterpret_cast<const float2*>(p);
+  else
+    return make_float2(*p, 0.0f);
+}
+
+template <int DT, int HD>
 __global__ __launch_bounds__(64 * COMBINE_ROWS) void fa_combine_kernel(
     const float* __restrict__ o_part, const float* __restrict__ lse_part,
     uint16_t* __restrict__ o, float* __restrict__ lse, int rows, int num_splits) {
+  constexpr int D = HD, CPL = HD / 64;  // columns per lane
   const int lane = threadIdx.x & 63;
   const unsigned r = blockIdx.x * COMBINE_ROWS + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (r >= (unsigned)rows) return;
   const float* ls = lse_part + (size_t)r * num_splits;
-  const float* op = o_part + (size_t)r * num_splits * D + 2 * lane;
+  const float* op = o_part + (size_t)r * num_splits * D + CPL * lane;
   float M = -INFINITY, L = 0.0f, a0 = 0.0f, a1 = 0.0f;
   // merge n splits starting at s whose LSEs are lv and outputs x
   auto merge = [&](const float* lv, const float2* x, int n) {
@@ -198,50 +218,62 @@ __global__ __launch_bounds__(64 * COMBINE_ROWS) void fa_combine_kernel(
     float2 x[COMBINE_BLOCK];
 #pragma unroll
     for (int i = 0; i < COMBINE_BLOCK; ++i)
-      x[i] = *reinterpret_cast<const float2*>(op + (size_t)(s + i) * D);
+      x[i] = load_cols<HD>(op + (size_t)(s + i) * D);
 #pragma unroll
     for (int i = 0; i < COMBINE_BLOCK; ++i) lv[i] = ls[s + i];
     merge(lv, x, COMBINE_BLOCK);
   }
   for (; s < num_splits; ++s) {
     const float lv = ls[s];
-    const float2 x = *reinterpret_cast<const float2*>(op + (size_t)s * D);
+    const float2 x = load_cols<HD>(op + (size_t)s * D);
     merge(&lv, &x, 1);
   }
   if (L > 0.0f) {
     a0 /= L;
     a1 /= L;
   }
-  *reinterpret_cast<unsigned*>(o + (size_t)r * D + 2 * lane) = pack2<DT>(a0, a1);
+  if constexpr (CPL == 2) {
+    *reinterpret_cast<unsigned*>(o + (size_t)r * D + 2 * lane) = pack2<DT>(a0, a1);
+  } else {
+    const unsigned w = pack2<DT>(a0, 0.0f);
+    o[(size_t)r * D + lane] = (uint16_t)(w & 0xffffu);
+  }
   if (lse != nullptr && lane == 0) lse[r] = (M == -INFINITY) ? -INFINITY : M + __logf(L);
 }
 
-constexpr unsigned DECODE_LDS_BYTES = 4 * TILE_BYTES;  // 2 tiles used; see the kernel
+// 64 KiB at either head dimension (two tiles, 32 or 16 KiB, are used; see the kernel)
+constexpr unsigned DECODE_LDS_BYTES = 4 * Geom<128>::TILE;
+
+template <int DT, int HD>
+static void launch_decode_split_t(const DecodeArgs& a, hipStream_t stream) {
+  const long long items = (long long)a.B * a.Hkv * a.num_splits;
+  hipLaunchKernelGGL((fa_decode_split_kernel<DT, HD>), dim3((unsigned)items), dim3(64),
+                     DECODE_LDS_BYTES, stream, static_cast<const uint16_t*>(a.q),
+                     static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
+                     a.o_part, a.lse_part, a.Hq, a.Hkv, a.Sk, a.num_splits, a.scale_log2);
+}
 
 hipError_t launch_decode_split(const DecodeArgs& a, hipStream_t stream) {
-  const long long items = (long long)a.B * a.Hkv * a.num_splits;
-  dim3 grid((unsigned)items), block(64);
-  auto q = static_cast<const uint16_t*>(a.q);
-  auto k = static_cast<const uint16_t*>(a.k);
-  auto v = static_cast<const uint16_t*>(a.v);
-  if (a.dtype == 0)
-    hipLaunchKernelGGL((fa_decode_split_kernel<0>), grid, block, DECODE_LDS_BYTES, stream, q, k,
-                       v, a.o_part, a.lse_part, a.Hq, a.Hkv, a.Sk, a.num_splits, a.scale_log2);
+  if (a.d == 64)
+    a.dtype == 0 ? launch_decode_split_t<0, 64>(a, stream) : launch_decode_split_t<1, 64>(a, stream);
   else
-    hipLaunchKernelGGL((fa_decode_split_kernel<1>), grid, block, DECODE_LDS_BYTES, stream, q, k,
-                       v, a.o_part, a.lse_part, a.Hq, a.Hkv, a.Sk, a.num_splits, a.scale_log2);
+    a.dtype == 0 ? launch_decode_split_t<0, 128>(a, stream)
+                 : launch_decode_split_t<1, 128>(a, stream);
   return hipGetLastError();
 }
 
-hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
+template <int DT, int HD>
+static void launch_combine_t(const CombineArgs& a, hipStream_t stream) {
   dim3 grid((unsigned)((a.rows + COMBINE_ROWS - 1) / COMBINE_ROWS)), block(64 * COMBINE_ROWS);
-  auto o = static_cast<uint16_t*>(a.o);
-  if (a.dtype == 0)
-    hipLaunchKernelGGL((fa_combine_kernel<0>), grid, block, 0, stream, a.o_part, a.lse_part, o,
-                       a.lse, a.rows, a.num_splits);
+  hipLaunchKernelGGL((fa_combine_kernel<DT, HD>), grid, block, 0, stream, a.o_part, a.lse_part,
+                     static_cast<uint16_t*>(a.o), a.lse, a.rows, a.num_splits);
+}
+
+hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
+  if (a.d == 64)
+    a.dtype == 0 ? launch_combine_t<0, 64>(a, stream) : launch_combine_t<1, 64>(a, stream);
   else
-    hipLaunchKernelGGL((fa_combine_kernel<1>), grid, block, 0, stream, a.o_part, a.lse_part, o,
-                       a.lse, a.rows, a.num_splits);
+    a.dtype == 0 ? launch_combine_t<0, 128>(a, stream) : launch_combine_t<1, 128>(a, stream);
   return hipGetLastError();
 }
 

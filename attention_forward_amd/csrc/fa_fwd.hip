@@ -28,7 +28,7 @@
 
 namespace attn {
 
-template <int DT>
+template <int DT, int HD>
 __global__ __launch_bounds__(FWD_NW * 64, 2) void fa_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ o, float* __restrict__ lse, int Hq, int Hkv, int Sq, int Sk, int causal,
@@ -38,6 +38,8 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fa_fwd_kernel(
   constexpr int BR = FWD_BR;
   static_assert(NW == 8 && FWD_QB == 1, "two groups of four single-block waves");
   // LDS: K stages at [0, 2 tiles), V stages at [2 tiles, 4 tiles)
+  using G = Geom<HD>;
+  constexpr int D = HD, ROW = G::ROW, TILE_BYTES = G::TILE;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * TILE_BYTES];
 
   const int lane = threadIdx.x & 63;
@@ -79,30 +81,32 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fa_fwd_kernel(
 
   // Q^T operands: lane holds Q[row][16*st + 8*g .. +7] for its query n; rows
   // past Sq read as zeros
-  u32x4 qf[QB][8];
+  u32x4 qf[QB][G::DSTEPS];
   {
     const __amdgpu_buffer_rsrc_t qr = make_rsrc(qh, (long long)Sq * ROW);
     const unsigned row_off = (unsigned)((qw0 + n) * ROW + 16 * g);
 #pragma unroll
-    for (int st = 0; st < 8; ++st) qf[0][st] = load_b128(qr, row_off + 32 * st);
+    for (int st = 0; st < G::DSTEPS; ++st) qf[0][st] = load_b128(qr, row_off + 32 * st);
     vm_wait_all();  // Q is in registers before any tile load is issued
   }
 
-  f32x16 acc[4][QB];
+  f32x16 acc[G::DBLOCKS][QB];
   float m[QB], l[QB];
   m[0] = -INFINITY;
   l[0] = 0.0f;
 #pragma unroll
-  for (int db = 0; db < 4; ++db) acc[db][0] = f32x16{};
+  for (int db = 0; db < G::DBLOCKS; ++db) acc[db][0] = f32x16{};
 
   // The loading waves split every tile: with L of them, chunk L*c + w covers
   // rows 4(L*c + w) + lane/16 (w = the wave's index among the loaders); L*c*4
   // is a multiple of 16 rows, so one swizzle pattern (and one lane offset)
   // serves all of a wave's chunks
   constexpr int LOADERS = ATTN_LOADERS == 2 ? NW : NW / 2;
-  constexpr int CHUNKS_PER_LOADER = (KT / 4) / LOADERS;
-  const unsigned koff = load_lane_offset<false>(wave & (LOADERS - 1));
-  const unsigned voff = load_lane_offset<true>(wave & (LOADERS - 1));
+  constexpr int CHUNKS_PER_LOADER = G::CHUNKS / LOADERS;
+  static_assert(CHUNKS_PER_LOADER * LOADERS == G::CHUNKS && (LOADERS * G::RPC) % 16 == 0,
+                "whole chunks per loader, 16-row strides");
+  const unsigned koff = load_lane_offset<HD, false>(wave & (LOADERS - 1));
+  const unsigned voff = load_lane_offset<HD, true>(wave & (LOADERS - 1));
   unsigned char ATTN_LDS* lds = (unsigned char ATTN_LDS*)(smem);
   auto issue = [&](const uint16_t* head, unsigned lane_off, int j, unsigned char ATTN_LDS* dst) {
     const int key0 = j * KT;
@@ -111,12 +115,12 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fa_fwd_kernel(
         make_rsrc(head + (size_t)key0 * D, (long long)(Sk - key0) * ROW);
 #pragma unroll
     for (int c = 0; c < CHUNKS_PER_LOADER; ++c)
-      load_chunk(r, lane_off + c * LOADERS * 4 * ROW,
+      load_chunk(r, lane_off + c * LOADERS * 1024,
                  dst + (c * LOADERS + (wave & (LOADERS - 1))) * 1024);
   };
   auto k_stage = [&](int j) { return lds + (j & 1) * TILE_BYTES; };
   auto v_stage = [&](int j) { return lds + (2 + (j & 1)) * TILE_BYTES; };
-  const LaneAddr la = lane_addresses();
+  const LaneAddr la = lane_addresses<HD>();
   const unsigned lds_base = (unsigned)(size_t)lds;
 
   f32x16 s[2][QB];
@@ -211,7 +215,7 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fa_fwd_kernel(
   if (n_wave > 0) {
     mfma_begin(0);
     prio_hi();
-    qk_step<DT, QB>(k_addr(0), la, qf, s);
+    qk_step<DT, QB, HD>(k_addr(0), la, qf, s);
     prio_lo();
     mfma_end();
     barrier();
@@ -222,8 +226,8 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fa_fwd_kernel(
     for (j = 1; j < n_wave; ++j) {
       mfma_begin(j);
       prio_hi();
-      pv_step<DT, QB>(v_addr(j - 1), la, pf, acc);
-      qk_step<DT, QB>(k_addr(j), la, qf, s);
+      pv_step<DT, QB, HD>(v_addr(j - 1), la, pf, acc);
+      qk_step<DT, QB, HD>(k_addr(j), la, qf, s);
       prio_lo();
       mfma_end();
       barrier();
@@ -233,7 +237,7 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fa_fwd_kernel(
       barrier();
       if (moved) {
 #pragma unroll
-        for (int db = 0; db < 4; ++db) acc[db][0] *= alpha[0];
+        for (int db = 0; db < G::DBLOCKS; ++db) acc[db][0] *= alpha[0];
         ++j;
         break;
       }
@@ -241,8 +245,8 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fa_fwd_kernel(
     for (; j < n_wave; ++j) {
       mfma_begin(j);
       prio_hi();
-      pv_step<DT, QB>(v_addr(j - 1), la, pf, acc);
-      qk_step<DT, QB>(k_addr(j), la, qf, s);
+      pv_step<DT, QB, HD>(v_addr(j - 1), la, pf, acc);
+      qk_step<DT, QB, HD>(k_addr(j), la, qf, s);
       prio_lo();
       mfma_end();
       barrier();
@@ -253,7 +257,7 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fa_fwd_kernel(
     }
     mfma_begin(j);
     prio_hi();
-    pv_step<DT, QB>(v_addr(j - 1), la, pf, acc);
+    pv_step<DT, QB, HD>(v_addr(j - 1), la, pf, acc);
     prio_lo();
     mfma_end();
     barrier();
@@ -280,7 +284,7 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fa_fwd_kernel(
     if (row < Sq) {
       uint16_t* orow = o + ((size_t)bh * Sq + row) * D;
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
+      for (int db = 0; db < G::DBLOCKS; ++db)
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
           const int d0 = 32 * db + 8 * jj + 4 * g;
@@ -296,21 +300,23 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fa_fwd_kernel(
   }
 }
 
-hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
+template <int DT, int HD>
+static void launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
   const int n_bh = a.B * a.Hq;
   const int n_qt = (a.Sq + FWD_BR - 1) / FWD_BR;
   const long long items = (long long)n_bh * n_qt;
   dim3 grid((unsigned)items), block(FWD_NW * 64);
-  auto q = static_cast<const uint16_t*>(a.q);
-  auto k = static_cast<const uint16_t*>(a.k);
-  auto v = static_cast<const uint16_t*>(a.v);
-  auto o = static_cast<uint16_t*>(a.o);
-  if (a.dtype == 0)
-    hipLaunchKernelGGL((fa_fwd_kernel<0>), grid, block, 0, stream, q, k, v, o, a.lse, a.Hq,
-                       a.Hkv, a.Sq, a.Sk, a.causal, a.scale_log2, n_bh, n_qt);
+  hipLaunchKernelGGL((fa_fwd_kernel<DT, HD>), grid, block, 0, stream,
+                     static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                     static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.lse, a.Hq,
+                     a.Hkv, a.Sq, a.Sk, a.causal, a.scale_log2, n_bh, n_qt);
+}
+
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
+  if (a.d == 64)
+    a.dtype == 0 ? launch_fwd_t<0, 64>(a, stream) : launch_fwd_t<1, 64>(a, stream);
   else
-    hipLaunchKernelGGL((fa_fwd_kernel<1>), grid, block, 0, stream, q, k, v, o, a.lse, a.Hq,
-                       a.Hkv, a.Sq, a.Sk, a.causal, a.scale_log2, n_bh, n_qt);
+    a.dtype == 0 ? launch_fwd_t<0, 128>(a, stream) : launch_fwd_t<1, 128>(a, stream);
   return hipGetLastError();
 }
 

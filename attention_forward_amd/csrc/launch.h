@@ -7,7 +7,8 @@
 
 namespace attn {
 
-constexpr int HEAD_DIM = 128;  // the head dimension the kernels implement
+// the head dimensions the kernels implement
+constexpr bool head_dim_supported(int d) { return d == 64 || d == 128; }
 
 struct FwdArgs {
   const void* q;
@@ -15,7 +16,7 @@ struct FwdArgs {
   const void* v;
   void* o;
   float* lse;
-  int B, Hq, Hkv, Sq, Sk;
+  int B, Hq, Hkv, Sq, Sk, d;
   int causal;
   float scale_log2;  // scale * log2(e), rounded once to fp32 on the host
   int dtype;
@@ -25,9 +26,9 @@ struct DecodeArgs {
   const void* q;
   const void* k;
   const void* v;
-  float* o_part;    // [B, Hq, num_splits, D] fp32
+  float* o_part;    // [B, Hq, num_splits, d] fp32
   float* lse_part;  // [B, Hq, num_splits] fp32, natural log
-  int B, Hq, Hkv, Sk;
+  int B, Hq, Hkv, Sk, d;
   int num_splits;
   float scale_log2;
   int dtype;
@@ -40,6 +41,7 @@ struct CombineArgs {
   float* lse;
   int rows;  // B * Hq
   int num_splits;
+  int d;
   int dtype;
 };
 

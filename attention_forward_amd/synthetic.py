@@ -62,6 +62,17 @@ WORKLOADS = {
         num_splits=16),
 }
 
+# The same shapes at head dimension 64 (the pages' other head dimension): the
+# headline prefill workload and the decode workload.
+HEAD_DIM_64_WORKLOADS = {
+    "fwd_bf16_causal_b2_h16_s8192_d64": Workload("fwd_bf16_causal_b2_h16_s8192_d64", 2, 16, 16,
+                                                 8192, 8192, 64, BF16, True, 6),
+    "decode_bf16_b64_hq32_hkv8_sk8192_split16_d64": Workload(
+        "decode_bf16_b64_hq32_hkv8_sk8192_split16_d64", 64, 32, 8, 1, 8192, 64, BF16, False, 7,
+        num_splits=16),
+}
+ALL_WORKLOADS = {**WORKLOADS, **HEAD_DIM_64_WORKLOADS}
+
 
 def _fill(shape, gen, dtype) -> torch.Tensor:
     out = torch.empty(shape, dtype=TORCH_DTYPE[dtype])

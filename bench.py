@@ -33,7 +33,8 @@ import numpy as np
 import torch
 
 import attention_forward_amd as A
-from attention_forward_amd.synthetic import BF16, WORKLOADS, bits, make_workload_inputs
+from attention_forward_amd.synthetic import (ALL_WORKLOADS, BF16, WORKLOADS, bits,
+                                             make_workload_inputs)
 
 PREFILL = WORKLOADS["fwd_bf16_causal_b2_h16_s8192"]
 DECODE = WORKLOADS["decode_bf16_b64_hq32_hkv8_sk8192_split16"]
@@ -144,18 +145,29 @@ def hbm_read_ceiling(gib=4, iters=10):
 
 
 def other_workloads(iters=5):
-    """Prefill TFLOP/s of the other prefill workloads (context; their parity is
-    checked by the GPU tests)."""
+    """Throughput of the other workloads (context; their parity is checked by the
+    GPU tests): the other prefill shapes in TFLOP/s, and the headline prefill
+    and decode shapes at head dimension 64 (TFLOP/s, GB/s)."""
     out = {}
-    for name, w in WORKLOADS.items():
-        if w.decode or w is PREFILL:
+    for name, w in ALL_WORKLOADS.items():
+        if w is PREFILL or w is DECODE:
             continue
         q, k, v = [t.cuda() for t in make_workload_inputs(w)]
         o = torch.empty_like(q)
-        lse = torch.empty(q.shape[:3], device="cuda", dtype=torch.float32)
-        ms = _time_ms(lambda: A.attn_fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse),
-                      iters, warmup=2)
-        out[name] = {"ms": round(ms, 4), "tflops": round(w.flops / (ms * 1e-3) / 1e12, 2)}
+        if w.decode:
+            lse = torch.empty((w.B, w.Hq), device="cuda", dtype=torch.float32)
+            ws = torch.empty(A.attn_decode_workspace_bytes(w.B, w.Hq, w.d, w.num_splits),
+                             device="cuda", dtype=torch.uint8)
+            ms = _time_ms(lambda: A.attn_fwd_decode(q, k, v, w.num_splits, scale=w.scale, out=o,
+                                                    lse=lse, workspace=ws), iters, warmup=2)
+            out[name] = {"ms": round(ms, 4),
+                         "gbs": round(decode_algorithmic_bytes(w) / (ms * 1e-3) / 1e9, 1)}
+            del ws
+        else:
+            lse = torch.empty(q.shape[:3], device="cuda", dtype=torch.float32)
+            ms = _time_ms(lambda: A.attn_fwd(q, k, v, causal=w.causal, scale=w.scale, out=o,
+                                             lse=lse), iters, warmup=2)
+            out[name] = {"ms": round(ms, 4), "tflops": round(w.flops / (ms * 1e-3) / 1e12, 2)}
         del q, k, v, o, lse
     return out
 

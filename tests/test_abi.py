@@ -63,7 +63,8 @@ def fwd(L, **kw):
 @cpu_only
 @pytest.mark.parametrize("kw,status", [
     (dict(B=0), A.ATTN_ERR_SHAPE), (dict(Sq=-1), A.ATTN_ERR_SHAPE), (dict(Sk=0), A.ATTN_ERR_SHAPE),
-    (dict(Hq=3, Hkv=2), A.ATTN_ERR_SHAPE), (dict(d=64), A.ATTN_ERR_UNSUPPORTED),
+    (dict(Hq=3, Hkv=2), A.ATTN_ERR_SHAPE), (dict(d=96), A.ATTN_ERR_UNSUPPORTED),
+    (dict(d=32), A.ATTN_ERR_UNSUPPORTED), (dict(d=64), A.ATTN_ERR_NO_DEVICE),
     (dict(dtype=2), A.ATTN_ERR_UNSUPPORTED), (dict(causal=2), A.ATTN_ERR_VALUE),
     (dict(scale=-1.0), A.ATTN_ERR_VALUE), (dict(scale=float("nan")), A.ATTN_ERR_VALUE),
     (dict(scale=float("inf")), A.ATTN_ERR_VALUE),
@@ -93,6 +94,7 @@ def dec(L, **kw):
     (dict(ns=0), A.ATTN_ERR_VALUE), (dict(ns=101), A.ATTN_ERR_VALUE),
     (dict(wsb=16), A.ATTN_ERR_WORKSPACE), (dict(ws=None), A.ATTN_ERR_WORKSPACE),
     (dict(ws=ctypes.c_void_p((1 << 20) + 4)), A.ATTN_ERR_ALIGN), (dict(d=256), A.ATTN_ERR_UNSUPPORTED),
+    (dict(d=64), A.ATTN_ERR_NO_DEVICE),
     (dict(scale=-0.5), A.ATTN_ERR_VALUE), (dict(Sk=1 << 24, ns=4), A.ATTN_ERR_SHAPE),
     (dict(), A.ATTN_ERR_NO_DEVICE),
 ])
@@ -106,6 +108,8 @@ def test_combine_validation(L):
     assert L.attn_splitkv_combine(P, P, P, None, 1, 1, 128, 2, 5, None) == A.ATTN_ERR_UNSUPPORTED
     assert L.attn_splitkv_combine(P, P, P, None, 0, 1, 128, 2, 0, None) == A.ATTN_ERR_SHAPE
     assert L.attn_splitkv_combine(P, P, P, None, 1, 1, 128, 2, 0, None) == A.ATTN_ERR_NO_DEVICE
+    assert L.attn_splitkv_combine(P, P, P, None, 1, 1, 64, 2, 0, None) == A.ATTN_ERR_NO_DEVICE
+    assert L.attn_splitkv_combine(P, P, P, None, 1, 1, 80, 2, 0, None) == A.ATTN_ERR_UNSUPPORTED
 
 
 def test_workspace_size(L):

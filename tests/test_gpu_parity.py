@@ -25,7 +25,8 @@ import torch
 
 import oracle
 from attention_forward_amd import attn_fwd, attn_fwd_decode, attn_splitkv_combine
-from attention_forward_amd.synthetic import BF16, F16, TORCH_DTYPE, WORKLOADS, bits, make_qkv
+from attention_forward_amd.synthetic import (ALL_WORKLOADS, BF16, F16, TORCH_DTYPE, bits,
+                                             make_qkv)
 
 pytestmark = pytest.mark.gpu
 
@@ -93,43 +94,59 @@ SMALL = [
 ]
 
 
-@pytest.mark.parametrize("shape", SMALL, ids=lambda s: "B%d_Hq%d_Hkv%d_Sq%d_Sk%d_%s_%s" % (
-    s[0], s[1], s[2], s[3], s[4], "bf16" if s[5] else "f16", "causal" if s[6] else "full"))
+SMALL_D64 = [
+    # B, Hq, Hkv, Sq, Sk, dtype, causal -- head dimension 64
+    (1, 1, 1, 1, 1, F16, False),
+    (1, 2, 2, 64, 64, BF16, False),
+    (1, 2, 2, 333, 333, BF16, True),
+    (2, 8, 2, 130, 257, F16, False),
+    (1, 4, 1, 100, 300, BF16, True),
+    (1, 2, 2, 300, 100, F16, True),
+    (1, 2, 2, 1, 700, BF16, False),
+    (2, 4, 4, 640, 640, BF16, True),
+]
+
+
+@pytest.mark.parametrize("shape", [s + (128,) for s in SMALL] + [s + (64,) for s in SMALL_D64],
+                         ids=lambda s: "B%d_Hq%d_Hkv%d_Sq%d_Sk%d_%s_%s_d%d" % (
+    s[0], s[1], s[2], s[3], s[4], "bf16" if s[5] else "f16", "causal" if s[6] else "full", s[7]))
 def test_small_shapes_all_rows(shape):
-    B, Hq, Hkv, Sq, Sk, dtype, causal = shape
+    B, Hq, Hkv, Sq, Sk, dtype, causal, d = shape
     name = "small %s" % (shape,)
     say("case", name)
-    q, k, v = make_qkv(B, Hq, Hkv, Sq, Sk, 128, dtype, seed=100 + Sq + Sk)
-    scale = 1.0 / math.sqrt(128)
+    q, k, v = make_qkv(B, Hq, Hkv, Sq, Sk, d, dtype, seed=100 + Sq + Sk + d)
+    scale = 1.0 / math.sqrt(d)
     o_gpu, lse_gpu = gpu_fwd(q, k, v, causal, scale, dtype)
     o, lse, o_ref = oracle.attention(bits(q), bits(k), bits(v), dtype, causal, scale)
     n = B * Hq * Sq
-    gate(o_gpu.to(torch.float64).numpy().reshape(n, 128), o.reshape(n, 128),
-         o_ref.reshape(n, 128), name=name)
+    gate(o_gpu.to(torch.float64).numpy().reshape(n, d), o.reshape(n, d), o_ref.reshape(n, d),
+         name=name)
     check_lse(lse_gpu.to(torch.float64).numpy().reshape(-1), lse.reshape(-1), name)
     if causal and Sq > Sk:
         hidden = o_gpu[:, :, : Sq - Sk]
         assert torch.all(hidden == 0), "fully masked rows must be exactly zero"
 
 
+@pytest.mark.parametrize("d", [128, 64])
 @pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
 @pytest.mark.parametrize("dtype", [F16, BF16], ids=["f16", "bf16"])
-def test_growing_scores_move_the_reference_max(dtype, causal):
+def test_growing_scores_move_the_reference_max(dtype, causal, d):
     """Key norms grow sixfold along the sequence, so later tiles' scores pass
     the first tile's maximum by far more than the rescale threshold: the
     reference max moves mid-loop and O must be rescaled from then on."""
     B, H, S = 1, 2, 1000
-    name = "growing scores %s %s" % ("bf16" if dtype else "f16", "causal" if causal else "full")
+    name = "growing scores %s %s d%d" % ("bf16" if dtype else "f16",
+                                         "causal" if causal else "full", d)
     say("case", name)
-    q, k, v = make_qkv(B, H, H, S, S, 128, dtype, seed=77)
-    ramp = torch.linspace(1.0, 6.0, S).view(1, 1, S, 1)
+    q, k, v = make_qkv(B, H, H, S, S, d, dtype, seed=77)
+    ramp = torch.linspace(1.0, 6.0, S).view(1, 1, S, 1)  # q.k / sqrt(d) has unit variance
     k = (k.float() * ramp).to(TORCH_DTYPE[dtype])
-    scale = 1.0 / math.sqrt(128)
+    scale = 1.0 / math.sqrt(d)
     o_gpu, lse_gpu = gpu_fwd(q, k, v, causal, scale, dtype)
     o, lse, o_ref = oracle.attention(bits(q), bits(k), bits(v), dtype, causal, scale)
     n = B * H * S
-    gate(o_gpu.to(torch.float64).numpy().reshape(n, 128), o.reshape(n, 128),
-         o_ref.reshape(n, 128), name=name)
+    gate(o_gpu.to(torch.float64).numpy().reshape(n, d), o.reshape(n, d), o_ref.reshape(n, d),
+         name=name)
     check_lse(lse_gpu.to(torch.float64).numpy().reshape(-1), lse.reshape(-1), name)
 
 
@@ -146,9 +163,9 @@ def sample_rows(B, H, S, rng, n_random):
     return np.unique(np.array(rows, dtype=np.int64))
 
 
-@pytest.mark.parametrize("wname", [w for w in WORKLOADS if not WORKLOADS[w].decode])
+@pytest.mark.parametrize("wname", [w for w in ALL_WORKLOADS if not ALL_WORKLOADS[w].decode])
 def test_workload_fwd(wname):
-    w = WORKLOADS[wname]
+    w = ALL_WORKLOADS[wname]
     say("case workload", wname)
     q, k, v = make_qkv(w.B, w.Hq, w.Hkv, w.Sq, w.Sk, w.d, w.dtype, w.seed)
     o_gpu, lse_gpu = gpu_fwd(q, k, v, w.causal, w.scale, w.dtype)
@@ -170,8 +187,9 @@ def test_workload_fwd(wname):
     check_lse(lse_gpu.reshape(-1)[torch.from_numpy(rows)].double().numpy(), lse, wname)
 
 
-def test_workload_decode():
-    w = WORKLOADS["decode_bf16_b64_hq32_hkv8_sk8192_split16"]
+@pytest.mark.parametrize("wname", [w for w in ALL_WORKLOADS if ALL_WORKLOADS[w].decode])
+def test_workload_decode(wname):
+    w = ALL_WORKLOADS[wname]
     say("case workload", w.name)
     q, k, v = make_qkv(w.B, w.Hq, w.Hkv, 1, w.Sk, w.d, w.dtype, w.seed)
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
@@ -198,33 +216,43 @@ DECODE_SMALL = [
     (2, 12, 4, 777, 5, BF16),
     (2, 8, 8, 40, 32, F16),  # splits 20..31 hold no keys
 ]
+DECODE_SMALL_D64 = [
+    (1, 1, 1, 1, 1, F16),
+    (2, 8, 2, 1000, 16, BF16),
+    (1, 32, 1, 513, 7, BF16),
+    (3, 16, 2, 64, 64, F16),
+    (2, 8, 8, 40, 32, BF16),
+]
 
 
-@pytest.mark.parametrize("shape", DECODE_SMALL, ids=lambda s: "B%d_Hq%d_Hkv%d_Sk%d_ns%d" % s[:5])
+@pytest.mark.parametrize("shape", [s + (128,) for s in DECODE_SMALL] +
+                         [s + (64,) for s in DECODE_SMALL_D64],
+                         ids=lambda s: "B%d_Hq%d_Hkv%d_Sk%d_ns%d_d%d" % (s[:5] + s[6:]))
 def test_decode_small(shape):
-    B, Hq, Hkv, Sk, ns, dtype = shape
+    B, Hq, Hkv, Sk, ns, dtype, d = shape
     say("case decode", shape)
-    q, k, v = make_qkv(B, Hq, Hkv, 1, Sk, 128, dtype, seed=200 + Sk)
-    scale = 1.0 / math.sqrt(128)
-    o = torch.full((B, Hq, 1, 128), float("nan"), device="cuda", dtype=TORCH_DTYPE[dtype])
+    q, k, v = make_qkv(B, Hq, Hkv, 1, Sk, d, dtype, seed=200 + Sk + d)
+    scale = 1.0 / math.sqrt(d)
+    o = torch.full((B, Hq, 1, d), float("nan"), device="cuda", dtype=TORCH_DTYPE[dtype])
     lse = torch.full((B, Hq), float("nan"), device="cuda")
     attn_fwd_decode(q.cuda(), k.cuda(), v.cuda(), ns, scale=scale, out=o, lse=lse)
     torch.cuda.synchronize()
     o_, lse_, o_ref = oracle.attention(bits(q), bits(k), bits(v), dtype, False, scale)
     n = B * Hq
-    gate(o.cpu().double().numpy().reshape(n, 128), o_.reshape(n, 128), o_ref.reshape(n, 128),
+    gate(o.cpu().double().numpy().reshape(n, d), o_.reshape(n, d), o_ref.reshape(n, d),
          np.ones(n, bool), name="decode %s" % (shape,))
     check_lse(lse.cpu().double().numpy().reshape(-1), lse_.reshape(-1), "decode")
 
 
+@pytest.mark.parametrize("d", [128, 64])
 @pytest.mark.parametrize("dtype", [F16, BF16])
 @pytest.mark.parametrize("S", [11, 16, 37, 70])
-def test_combine_matches_oracle(dtype, S):
+def test_combine_matches_oracle(dtype, S, d):
     """Split counts below, at and past whole blocks of merged splits, and past 64."""
-    say("case combine", dtype, S)
-    rng = np.random.default_rng(5 + S)
+    say("case combine", dtype, S, d)
+    rng = np.random.default_rng(5 + S + d)
     B, Hq = 3, 5
-    o_part = rng.standard_normal((B, Hq, S, 128))
+    o_part = rng.standard_normal((B, Hq, S, d))
     lse_part = rng.standard_normal((B, Hq, S)) * 3
     lse_part[0, 0, 3:] = -np.inf          # some empty splits
     lse_part[1, 2, :] = -np.inf           # a row with no keys at all
