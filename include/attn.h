@@ -46,7 +46,7 @@ typedef enum {
   ATTN_OK = 0,
   ATTN_ERR_NULL = 1,        /* a required pointer is NULL */
   ATTN_ERR_SHAPE = 2,       /* non-positive size, Hq % Hkv != 0, Sq or Sk >= 2^24, size overflow */
-  ATTN_ERR_UNSUPPORTED = 3, /* valid but not implemented: d != 128, dtype, GQA group > 32 */
+  ATTN_ERR_UNSUPPORTED = 3, /* valid but not implemented: d not 64 or 128, dtype, GQA group > 32 */
   ATTN_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
   ATTN_ERR_WORKSPACE = 5,   /* decode workspace missing or too small */
   ATTN_ERR_NO_DEVICE = 6,   /* no HIP device visible */
@@ -63,7 +63,7 @@ typedef enum {
  *              visible keys; may be NULL when not wanted.
  *   scale    : multiplies q.k before the softmax (usually 1/sqrt(d)); >= 0.
  *   causal   : 0 or 1.
- *   d        : head dimension; 128 is implemented.
+ *   d        : head dimension; 64 and 128 are implemented.
  * The exponentials run in base 2 with scale*log2(e) folded into one multiply
  * ("The FA5090 Optimization Journey", sec. 2.6; "G5: Pipeline ...", V33).
  */
@@ -87,7 +87,7 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int d, int num_splits);
  * as a way to spread one row's keys over more of the chip: "The FA5090
  * Optimization Journey", sec. 2.7.
  *   q, o     : [B,Hq,1,d]; k, v: [B,Hkv,Sk,d]; lse: fp32 [B,Hq] or NULL.
- *   num_splits in [1, Sk]; Hq/Hkv <= 32.
+ *   num_splits in [1, Sk]; Hq/Hkv <= 32; d is 64 or 128.
  *   workspace: device buffer of at least attn_decode_workspace_bytes(...)
  *              bytes, owned by the caller; its contents on entry are ignored.
  * Enqueues the split kernel, then the combine kernel, on `stream`.
@@ -103,7 +103,7 @@ int attn_fwd_decode(const void* q, const void* k, const void* v, void* o, float*
  * A row whose partial LSEs are all -inf gets O = 0 and LSE = -inf.  This is the
  * online-softmax merge of two running states applied across splits ("The FA5090
  * Optimization Journey", sec. 2.6, the running max and the final 1/l).
- *   o_part  : fp32 [B,Hq,num_splits,d], each partial already normalised.
+ *   o_part  : fp32 [B,Hq,num_splits,d], each partial already normalised; d is 64 or 128.
  *   lse_part: fp32 [B,Hq,num_splits], natural log.
  *   o       : [B,Hq,d] in dtype;  lse: fp32 [B,Hq] or NULL.
  */
