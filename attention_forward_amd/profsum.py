@@ -1,7 +1,7 @@
 """Summarise rocprofv3 CSV output into the short text summaries kept under profiles/.
 
     # kernel durations (rocprofv3 --kernel-trace --stats -f csv ... -o NAME)
-    python -m attention_forward_amd.profsum stats DIR NAME --cmd "<command>" > profiles/X.md
+    python -m attention_forward_amd.profsum stats DIR NAME --cmd "<command>" [--skip-first N] > profiles/X.md
 
     # HBM bytes per dispatch from two --pmc runs (FETCH_SIZE, WRITE_SIZE), each scaled by
     # what the same counter reads for a plain copy of --copy-mib MiB run in the same process
@@ -42,16 +42,37 @@ def short(name: str) -> str:
     return name if i < 0 else name[:i]
 
 
-def stats(d, name, cmd):
+def stats(d, name, cmd, skip_first=0):
+    """The --stats table, and (with skip_first) the same averages over each kernel's
+    dispatches after its first skip_first, from the kernel trace: the untimed
+    warmup steps of a benchmark run drop out, so the figures compare with the
+    benchmark's own timed-step averages."""
     path = os.path.join(d, name + "_kernel_stats.csv")
     rows = list(csv.DictReader(open(path)))
     out = ["# Kernel durations", "", "Command:", "", "```", cmd, "```", "",
+           "All dispatches (rocprofv3 --stats):", "",
            "| kernel | calls | average µs | min µs | max µs | share |",
            "|---|---|---|---|---|---|"]
     for r in rows:
         out.append("| `%s` | %s | %.1f | %.1f | %.1f | %.1f%% |" % (
             short(r["Name"]), r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
             float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+    if skip_first > 0:
+        trace = os.path.join(d, name + "_kernel_trace.csv")
+        per = collections.defaultdict(list)
+        for r in csv.DictReader(open(trace)):
+            per[short(r["Kernel_Name"])].append(
+                (int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+        out += ["", "Dispatches after each kernel's first %d (the untimed warmup steps):" %
+                skip_first, "", "| kernel | calls | average µs | median µs | min µs | max µs |",
+                "|---|---|---|---|---|---|"]
+        for k, v in per.items():
+            dur = sorted(x[1] for x in sorted(v)[skip_first:])
+            if not dur:
+                continue
+            out.append("| `%s` | %d | %.1f | %.1f | %.1f | %.1f |" % (
+                k, len(dur), sum(dur) / len(dur) / 1e3, dur[len(dur) // 2] / 1e3, dur[0] / 1e3,
+                dur[-1] / 1e3))
     return "\n".join(out) + "\n"
 
 
@@ -112,6 +133,8 @@ def main():
     s.add_argument("dir")
     s.add_argument("name")
     s.add_argument("--cmd", required=True)
+    s.add_argument("--skip-first", type=int, default=0,
+                   help="also average each kernel's dispatches after its first N")
     t = sub.add_parser("traffic")
     t.add_argument("dir")
     t.add_argument("fetch_name")
@@ -122,7 +145,7 @@ def main():
     t.add_argument("--out", default=None)
     a = ap.parse_args()
     if a.what == "stats":
-        sys.stdout.write(stats(a.dir, a.name, a.cmd))
+        sys.stdout.write(stats(a.dir, a.name, a.cmd, a.skip_first))
     else:
         sys.stdout.write(traffic(a.dir, a.fetch_name, a.write_name, a.copy_mib, a.cmd_fetch,
                                  a.cmd_write, a.out))
