@@ -52,11 +52,21 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 #define ATTN_LDS __attribute__((address_space(3)))
+// Build-time switches (defaults are the measured best):
+// ATTN_KDEPTH: K operand reads issued ahead of their MFMA.
+// ATTN_FAST_SOFTMAX: try the max-free form of the threshold rule first on
+//   tiles every row sees in full (softmax_fast).
+// ATTN_SETPRIO: raise the prefill MFMA phase's wave priority; with the
+//   shorter max-free softmax phase it measured 1-2% slower than leaving the
+//   two waves of a SIMD at equal priority.
 #ifndef ATTN_KDEPTH
 #define ATTN_KDEPTH 8
 #endif
+#ifndef ATTN_FAST_SOFTMAX
+#define ATTN_FAST_SOFTMAX 1
+#endif
 #ifndef ATTN_SETPRIO
-#define ATTN_SETPRIO 1
+#define ATTN_SETPRIO 0
 #endif
 
 // dtype 0: IEEE binary16, dtype 1: bfloat16
@@ -353,8 +363,9 @@ __device__ __forceinline__ bool softmax_step(f32x16 (&s)[2][QB], f32x16 (&o)[NDB
     float mxs = mx * scale_log2;
     if constexpr (MASK) mxs = (mx == -INFINITY) ? -INFINITY : mxs;
     const bool jump = mxs > m[qb] + TAU;
-    const float alpha =
-        jump ? ((m[qb] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m[qb] - mxs)) : 1.0f;
+    // exp2(0) = 1 exactly when m stays, exp2(-inf) = 0 when m leaves -inf; no
+    // branch, so the whole step stays one basic block for the scheduler
+    const float alpha = __builtin_amdgcn_exp2f(jump ? m[qb] - mxs : 0.0f);
     moved |= jump && m[qb] != -INFINITY;
     m[qb] = jump ? mxs : m[qb];
     l[qb] *= alpha;
@@ -395,6 +406,58 @@ __device__ __forceinline__ bool softmax_step(f32x16 (&s)[2][QB], f32x16 (&o)[NDB
     return false;
   else
     return __builtin_amdgcn_ballot_w64(moved) != 0;
+}
+
+// Fast form of the threshold rule for a tile that every row sees in full:
+// the weights are taken against the current reference max m, without the
+// row max.  Returns true, for the whole wave, when the tile must go through
+// softmax_step instead: some row's m is still -inf, or some weight may have
+// reached 2^(TAU - 1).  Otherwise no row's max exceeds m + TAU - 1, so
+// softmax_step would have kept m with alpha = 1, and l and pf now hold
+// exactly what it would have produced (same products, same exponentials,
+// same order of the row sum).
+//
+// The test needs no max: the row sum only grows as it adds non-negative
+// weights, so a weight p >= 2^(TAU - 1) leaves rs >= fl(l + p) >=
+// fl(l + 2^(TAU - 1)); rs below that bound thus rules out every such weight.
+// An infinite or NaN sum fails the test as well.  ("The FA5090 Optimization
+// Journey", sec. 3, threshold rescale; the bound on the weights is what keeps
+// the fp32 sums and the rounded P in range.)
+template <int DT, int QB>
+__device__ __forceinline__ bool softmax_fast(const f32x16 (&s)[2][QB], const float (&m)[QB],
+                                             float (&l)[QB], u32x4 (&pf)[2][2][QB],
+                                             float scale_log2) {
+  constexpr float BOUND = 128.0f;  // 2^(TAU - 1) with TAU = 8
+  bool bad = false;
+  float rs_q[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const float neg_m = -m[qb];
+    float rs = l[qb];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        u32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p0 =
+              __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][qb][8 * t + 2 * e], scale_log2, neg_m));
+          const float p1 = __builtin_amdgcn_exp2f(
+              __builtin_fmaf(s[kb][qb][8 * t + 2 * e + 1], scale_log2, neg_m));
+          rs += p0;
+          rs += p1;
+          w[e] = pack2<DT>(p0, p1);
+        }
+        pf[kb][t][qb] = w;
+      }
+    bad |= !(rs < l[qb] + BOUND);
+    rs_q[qb] = rs;
+  }
+  const bool redo = __builtin_amdgcn_ballot_w64(bad) != 0;
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) l[qb] = redo ? l[qb] : rs_q[qb];
+  return redo;
 }
 
 // O^T += V^T P^T: DBLOCKS d-blocks x 4 key steps, operands 4 steps ahead.

@@ -176,6 +176,7 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fa_fwd_kernel(
     if (masked(j))
       return softmax_step<DT, QB, true, false>(s, acc, m, l, pf, scale_log2, key0, qw0, Sk,
                                                causal != 0, causal_off, alpha);
+    if (ATTN_FAST_SOFTMAX && !softmax_fast<DT, QB>(s, m, l, pf, scale_log2)) return false;
     return softmax_step<DT, QB, false, false>(s, acc, m, l, pf, scale_log2, key0, qw0, Sk,
                                               false, 0, alpha);
   };
