@@ -31,7 +31,8 @@ ATTN_ERR_VALUE = 8
 ATTN_F16 = 0
 ATTN_BF16 = 1
 
-EXPORTED = ("attn_fwd", "attn_decode_workspace_bytes", "attn_fwd_decode", "attn_splitkv_combine",
+EXPORTED = ("attn_fwd", "attn_fwd_split", "attn_fwd_split_workspace_bytes", "attn_fwd_num_splits",
+            "attn_decode_workspace_bytes", "attn_fwd_decode", "attn_splitkv_combine",
             "attn_last_error")
 
 _lib = None
@@ -55,6 +56,12 @@ def lib() -> ctypes.CDLL:
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     L.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp]
     L.attn_fwd.restype = i
+    L.attn_fwd_split.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, i, vp, sz, vp]
+    L.attn_fwd_split.restype = i
+    L.attn_fwd_split_workspace_bytes.argtypes = [i, i, i, i, i]
+    L.attn_fwd_split_workspace_bytes.restype = sz
+    L.attn_fwd_num_splits.argtypes = [i, i, i, i, i]
+    L.attn_fwd_num_splits.restype = i
     L.attn_decode_workspace_bytes.argtypes = [i, i, i, i]
     L.attn_decode_workspace_bytes.restype = sz
     L.attn_fwd_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, sz, vp]
@@ -130,6 +137,53 @@ def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
     st = lib().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Sq, Sk, d,
                         1 if causal else 0, float(scale), _dtype_code(q), _stream(q.device))
+    _check(st)
+    return out, lse
+
+
+def attn_fwd_num_splits(B: int, Hq: int, Sq: int, Sk: int, d: int) -> int:
+    return int(lib().attn_fwd_num_splits(B, Hq, Sq, Sk, d))
+
+
+def attn_fwd_split_workspace_bytes(B: int, Hq: int, Sq: int, d: int, num_splits: int) -> int:
+    return int(lib().attn_fwd_split_workspace_bytes(B, Hq, Sq, d, num_splits))
+
+
+def attn_fwd_split(q, k, v, num_splits: int | None = None, causal: bool = False,
+                   scale: float | None = None, out=None, lse=None, workspace=None,
+                   want_lse: bool = True):
+    """Split-KV prefill: attn_fwd's result from num_splits key ranges merged by LSE.
+
+    num_splits defaults to attn_fwd_num_splits(...).  `workspace` (uint8 device
+    tensor of at least attn_fwd_split_workspace_bytes bytes) is allocated when
+    omitted.  Returns (o, lse) like attn_fwd.
+    """
+    import torch
+
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _require(t, nm)
+    B, Hq, Sq, d = q.shape
+    Bk, Hkv, Sk, dk = k.shape
+    if Bk != B or dk != d or tuple(v.shape) != tuple(k.shape):
+        raise AttnError(ATTN_ERR_SHAPE, "q %s / k %s / v %s shapes disagree"
+                        % (tuple(q.shape), tuple(k.shape), tuple(v.shape)))
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise AttnError(ATTN_ERR_UNSUPPORTED, "q, k, v must share one dtype")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if num_splits is None:
+        num_splits = attn_fwd_num_splits(B, Hq, Sq, Sk, d)
+    need = attn_fwd_split_workspace_bytes(B, Hq, Sq, d, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    st = lib().attn_fwd_split(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Sq, Sk,
+                              d, 1 if causal else 0, float(scale), _dtype_code(q), int(num_splits),
+                              _ptr(workspace), workspace.numel() * workspace.element_size(),
+                              _stream(q.device))
     _check(st)
     return out, lse
 

@@ -86,6 +86,85 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
   return hip_status(attn::launch_fwd(a, static_cast<hipStream_t>(stream)), "attn_fwd launch");
 }
 
+int attn_fwd_num_splits(int B, int Hq, int Sq, int Sk, int d) {
+  if (B <= 0 || Hq <= 0 || Sq <= 0 || Sk <= 0 || !attn::head_dim_supported(d)) return 1;
+  const long long items = (long long)B * Hq * ((Sq + attn::FWD_BR - 1) / attn::FWD_BR);
+  const int tiles = (Sk + attn::FWD_KT - 1) / attn::FWD_KT;
+  if (items >= attn::FWD_FILL_ITEMS) return 1;
+  // enough splits for one workgroup per compute unit, keeping at least two
+  // tiles per split (one-tile splits measured no faster: each split pays for
+  // its Q load and fp32 partial round trip)
+  const long long want = (attn::FWD_FILL_ITEMS + items - 1) / items;
+  const long long cap = tiles / 2 > 1 ? tiles / 2 : 1;
+  return (int)(want < cap ? want : cap);
+}
+
+size_t attn_fwd_split_workspace_bytes(int B, int Hq, int Sq, int d, int num_splits) {
+  if (B <= 0 || Hq <= 0 || Sq <= 0 || d <= 0 || num_splits <= 0) return 0;
+  const size_t rows = (size_t)B * Hq * Sq * num_splits;
+  return round_up(rows * d * sizeof(float)) + round_up(rows * sizeof(float));
+}
+
+int attn_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                   int Hq, int Hkv, int Sq, int Sk, int d, int causal, float scale, int dtype,
+                   int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = '\0';
+  if (!q || !k || !v || !o)
+    return fail(ATTN_ERR_NULL, "attn_fwd_split: q, k, v and o must be non-NULL");
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Sq <= 0 || Sk <= 0 || d <= 0)
+    return fail(ATTN_ERR_SHAPE,
+                "attn_fwd_split: sizes must be positive (B=%d Hq=%d Hkv=%d Sq=%d Sk=%d d=%d)", B,
+                Hq, Hkv, Sq, Sk, d);
+  if (Hq % Hkv != 0)
+    return fail(ATTN_ERR_SHAPE, "attn_fwd_split: Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  if (dtype != ATTN_F16 && dtype != ATTN_BF16)
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd_split: dtype %d is not 0 (fp16) or 1 (bf16)",
+                dtype);
+  if (!attn::head_dim_supported(d))
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd_split: head dim %d (64 and 128 are implemented)",
+                d);
+  if (causal != 0 && causal != 1)
+    return fail(ATTN_ERR_VALUE, "attn_fwd_split: causal must be 0 or 1");
+  if (!std::isfinite(scale) || scale < 0.0f)
+    return fail(ATTN_ERR_VALUE, "attn_fwd_split: scale must be finite and >= 0");
+  if (Sq > kMaxSeq || Sk > kMaxSeq)
+    return fail(ATTN_ERR_SHAPE, "attn_fwd_split: sequence length above %d", kMaxSeq);
+  const int tiles = (Sk + attn::FWD_KT - 1) / attn::FWD_KT;
+  if (num_splits < 1 || num_splits > tiles)
+    return fail(ATTN_ERR_VALUE, "attn_fwd_split: num_splits=%d not in [1, %d] (64-key tiles)",
+                num_splits, tiles);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+      (lse && !aligned4(lse)))
+    return fail(ATTN_ERR_ALIGN, "attn_fwd_split: q, k, v, o must be 16-byte aligned, lse 4-byte");
+  const size_t need = attn_fwd_split_workspace_bytes(B, Hq, Sq, d, num_splits);
+  if (!workspace || workspace_bytes < need)
+    return fail(ATTN_ERR_WORKSPACE, "attn_fwd_split: workspace of %zu bytes needed, %zu given",
+                need, workspace ? workspace_bytes : (size_t)0);
+  if (!aligned16(workspace)) return fail(ATTN_ERR_ALIGN, "attn_fwd_split: misaligned workspace");
+  const long long items =
+      (long long)B * Hq * ((Sq + attn::FWD_BR - 1) / attn::FWD_BR) * num_splits;
+  const long long rows = (long long)B * Hq * Sq;
+  if (items > INT_MAX || rows > INT_MAX || rows * d > (1LL << 46) ||
+      (long long)B * Hkv * Sk * d > (1LL << 46))
+    return fail(ATTN_ERR_SHAPE, "attn_fwd_split: problem too large for one launch");
+  int st = check_device();
+  if (st != ATTN_OK) return st;
+  const size_t prow = (size_t)rows * num_splits;
+  float* o_part = static_cast<float*>(workspace);
+  float* lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                             round_up(prow * d * sizeof(float)));
+  // split s covers keys [s * split_keys, (s + 1) * split_keys): whole tiles,
+  // as evenly as whole tiles allow (trailing splits may be short or empty)
+  const int split_keys = (tiles + num_splits - 1) / num_splits * attn::FWD_KT;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  attn::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, d, causal, fold_log2e(scale), dtype};
+  attn::FwdSplitArgs sa{o_part, lse_part, num_splits, split_keys};
+  st = hip_status(attn::launch_fwd_split(a, sa, hs), "attn_fwd_split partial launch");
+  if (st != ATTN_OK) return st;
+  attn::CombineArgs ca{o_part, lse_part, o, lse, (int)rows, num_splits, d, dtype};
+  return hip_status(attn::launch_combine(ca, hs), "attn_fwd_split combine launch");
+}
+
 size_t attn_decode_workspace_bytes(int B, int Hq, int d, int num_splits) {
   if (B <= 0 || Hq <= 0 || d <= 0 || num_splits <= 0) return 0;
   const size_t rows = (size_t)B * Hq * num_splits;

@@ -28,11 +28,22 @@
 
 namespace attn {
 
-template <int DT, int HD>
+static_assert(KT == FWD_KT, "the host's split arithmetic uses the kernels' tile");
+
+// PART: split-KV form for grids too small to fill the chip.  Work item
+// (q block, batch*head, split s) attends to keys [s * split_keys, (s + 1) *
+// split_keys) only and writes the normalised partial O in fp32 and its LSE
+// (natural log) to o_part [B*Hq*Sq, n_split, d] and lse_part [B*Hq*Sq,
+// n_split]; the split-KV combine merges them.  The kernel body is the same:
+// it sees K and V from the split's first key on, Sk cut to the split and the
+// causal offset shifted by the split's start.  A split with no visible key
+// writes O = 0 and LSE = -inf, which the combine weighs by 0.
+template <int DT, int HD, bool PART>
 __global__ __launch_bounds__(FWD_NW * 64, 2) void fa_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    uint16_t* __restrict__ o, float* __restrict__ lse, int Hq, int Hkv, int Sq, int Sk, int causal,
-    float scale_log2, int n_bh, int n_qt) {
+    uint16_t* __restrict__ o, float* __restrict__ lse, int Hq, int Hkv, int Sq, int Sk_all,
+    int causal, float scale_log2, int n_bh, int n_qt, float* __restrict__ o_part,
+    float* __restrict__ lse_part, int n_split, int split_keys) {
   constexpr int NW = FWD_NW;
   constexpr int QB = 1;
   constexpr int BR = FWD_BR;
@@ -48,7 +59,8 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fa_fwd_kernel(
   const int g = lane >> 5;
   const int n = lane & 31;
 
-  const int t = blockIdx.x;
+  const int sp = PART ? (int)(blockIdx.x % (unsigned)n_split) : 0;
+  const int t = PART ? (int)(blockIdx.x / (unsigned)n_split) : (int)blockIdx.x;
   const int rank = t / n_bh;
   const int bh = t - rank * n_bh;
   const int qt = causal ? (n_qt - 1 - rank) : rank;
@@ -56,10 +68,14 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fa_fwd_kernel(
   const int hq = bh - b * Hq;
   const int hkv = hq / (Hq / Hkv);
 
+  // keys [kv0, kv0 + Sk) of the head, indexed from kv0 below
+  const int kv0 = PART ? sp * split_keys : 0;
+  const int Sk = PART ? max(0, min(Sk_all - kv0, split_keys)) : Sk_all;
   const uint16_t* qh = q + (size_t)bh * Sq * D;
-  const uint16_t* kh = k + ((size_t)b * Hkv + hkv) * Sk * D;
-  const uint16_t* vh = v + ((size_t)b * Hkv + hkv) * Sk * D;
-  const int causal_off = Sk - Sq;
+  const uint16_t* kh = k + (((size_t)b * Hkv + hkv) * Sk_all + kv0) * D;
+  const uint16_t* vh = v + (((size_t)b * Hkv + hkv) * Sk_all + kv0) * D;
+  // key i (from kv0) is visible to row r iff i <= r + causal_off
+  const int causal_off = Sk_all - Sq - kv0;
 
   const int q0 = qt * BR;
   const int qw0 = q0 + wave * 32;  // this wave's first query row
@@ -278,7 +294,28 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fa_fwd_kernel(
   if (group_a) barrier();
 
   // epilogue: O = acc / l, rounded to the dtype; LSE = ln2 * (m + log2 l)
-  {
+  if constexpr (PART) {
+    const float lt = half_sum(l[0]);
+    const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+    const int row = qw0 + n;
+    if (row < Sq) {
+      const size_t prow = ((size_t)bh * Sq + row) * n_split + sp;
+      float* orow = o_part + prow * D;
+#pragma unroll
+      for (int db = 0; db < G::DBLOCKS; ++db)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int d0 = 32 * db + 8 * jj + 4 * g;
+          f32x4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = acc[db][0][4 * jj + e] * inv;
+          *reinterpret_cast<f32x4*>(orow + d0) = w;
+        }
+      if (g == 0)
+        lse_part[prow] =
+            lt > 0.0f ? 0.69314718055994531f * (m[0] + __builtin_amdgcn_logf(lt)) : -INFINITY;
+    }
+  } else {
     const float lt = half_sum(l[0]);
     const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
     const int row = qw0 + n;
@@ -301,24 +338,38 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fa_fwd_kernel(
   }
 }
 
-template <int DT, int HD>
-static void launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
+template <int DT, int HD, bool PART>
+static void launch_fwd_t(const FwdArgs& a, const FwdSplitArgs* sa, hipStream_t stream) {
   const int n_bh = a.B * a.Hq;
   const int n_qt = (a.Sq + FWD_BR - 1) / FWD_BR;
-  const long long items = (long long)n_bh * n_qt;
+  const int n_split = PART ? sa->num_splits : 1;
+  const long long items = (long long)n_bh * n_qt * n_split;
   dim3 grid((unsigned)items), block(FWD_NW * 64);
-  hipLaunchKernelGGL((fa_fwd_kernel<DT, HD>), grid, block, 0, stream,
+  hipLaunchKernelGGL((fa_fwd_kernel<DT, HD, PART>), grid, block, 0, stream,
                      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.lse, a.Hq,
-                     a.Hkv, a.Sq, a.Sk, a.causal, a.scale_log2, n_bh, n_qt);
+                     a.Hkv, a.Sq, a.Sk, a.causal, a.scale_log2, n_bh, n_qt,
+                     PART ? sa->o_part : nullptr, PART ? sa->lse_part : nullptr, n_split,
+                     PART ? sa->split_keys : 0);
+}
+
+template <bool PART>
+static hipError_t launch_fwd_any(const FwdArgs& a, const FwdSplitArgs* sa, hipStream_t stream) {
+  if (a.d == 64)
+    a.dtype == 0 ? launch_fwd_t<0, 64, PART>(a, sa, stream)
+                 : launch_fwd_t<1, 64, PART>(a, sa, stream);
+  else
+    a.dtype == 0 ? launch_fwd_t<0, 128, PART>(a, sa, stream)
+                 : launch_fwd_t<1, 128, PART>(a, sa, stream);
+  return hipGetLastError();
 }
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
-  if (a.d == 64)
-    a.dtype == 0 ? launch_fwd_t<0, 64>(a, stream) : launch_fwd_t<1, 64>(a, stream);
-  else
-    a.dtype == 0 ? launch_fwd_t<0, 128>(a, stream) : launch_fwd_t<1, 128>(a, stream);
-  return hipGetLastError();
+  return launch_fwd_any<false>(a, nullptr, stream);
+}
+
+hipError_t launch_fwd_split(const FwdArgs& a, const FwdSplitArgs& sa, hipStream_t stream) {
+  return launch_fwd_any<true>(a, &sa, stream);
 }
 
 }  // namespace attn

@@ -22,6 +22,15 @@ struct FwdArgs {
   int dtype;
 };
 
+// split-KV prefill: partial outputs of num_splits key ranges of split_keys
+// keys each (a multiple of the 64-key tile)
+struct FwdSplitArgs {
+  float* o_part;    // [B, Hq, Sq, num_splits, d] fp32
+  float* lse_part;  // [B, Hq, Sq, num_splits] fp32, natural log
+  int num_splits;
+  int split_keys;
+};
+
 struct DecodeArgs {
   const void* q;
   const void* k;
@@ -46,6 +55,7 @@ struct CombineArgs {
 };
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_fwd_split(const FwdArgs& a, const FwdSplitArgs& sa, hipStream_t stream);
 hipError_t launch_decode_split(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 
@@ -73,5 +83,9 @@ constexpr int FWD_QB = ATTN_FWD_QB;
 constexpr int FWD_NW = ATTN_FWD_NW;
 constexpr int FWD_WAVES_PER_SIMD = ATTN_FWD_WPE;  // occupancy the register budget is sized for
 constexpr int FWD_BR = FWD_QB * FWD_NW * 32;  // query rows per workgroup
+constexpr int FWD_KT = 64;                     // keys per K/V tile
+// prefill work items below which the split-KV form is recommended: one
+// workgroup per compute unit
+constexpr int FWD_FILL_ITEMS = 256;
 
 }  // namespace attn

@@ -168,6 +168,17 @@ def other_workloads(iters=5):
             ms = _time_ms(lambda: A.attn_fwd(q, k, v, causal=w.causal, scale=w.scale, out=o,
                                              lse=lse), iters, warmup=2)
             out[name] = {"ms": round(ms, 4), "tflops": round(w.flops / (ms * 1e-3) / 1e12, 2)}
+            # under-filled grids: the split-KV form with the recommended split count
+            ns = A.attn_fwd_num_splits(w.B, w.Hq, w.Sq, w.Sk, w.d)
+            if ns > 1:
+                ws = torch.empty(A.attn_fwd_split_workspace_bytes(w.B, w.Hq, w.Sq, w.d, ns),
+                                 device="cuda", dtype=torch.uint8)
+                ms = _time_ms(lambda: A.attn_fwd_split(q, k, v, ns, causal=w.causal,
+                                                       scale=w.scale, out=o, lse=lse,
+                                                       workspace=ws), iters, warmup=2)
+                out[name]["split"] = {"num_splits": ns, "ms": round(ms, 4),
+                                      "tflops": round(w.flops / (ms * 1e-3) / 1e12, 2)}
+                del ws
         del q, k, v, o, lse
     return out
 

@@ -48,7 +48,7 @@ typedef enum {
   ATTN_ERR_SHAPE = 2,       /* non-positive size, Hq % Hkv != 0, Sq or Sk >= 2^24, size overflow */
   ATTN_ERR_UNSUPPORTED = 3, /* valid but not implemented: d not 64 or 128, dtype, GQA group > 32 */
   ATTN_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
-  ATTN_ERR_WORKSPACE = 5,   /* decode workspace missing or too small */
+  ATTN_ERR_WORKSPACE = 5,   /* split workspace missing or too small */
   ATTN_ERR_NO_DEVICE = 6,   /* no HIP device visible */
   ATTN_ERR_HIP = 7,         /* a HIP call failed; see attn_last_error() */
   ATTN_ERR_VALUE = 8        /* bad scalar: causal not 0/1, scale negative or not finite,
@@ -70,6 +70,44 @@ typedef enum {
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int B, int Hq, int Hkv, int Sq, int Sk, int d, int causal, float scale,
              int dtype, void* stream);
+
+/*
+ * Split-KV prefill for grids too small to fill the chip (few batch*head
+ * pairs, short queries).  The same result as attn_fwd, up to rounding, computed
+ * by cutting the keys into num_splits ranges of whole 64-key tiles, as evenly as
+ * whole tiles allow (split s covers keys [s*c, (s+1)*c) with
+ * c = 64*ceil(ceil(Sk/64)/num_splits); trailing splits may be short or empty),
+ * attending to each range independently with fp32 partial outputs, and merging
+ * them by their LSEs (attn_splitkv_combine).  The pages measured split-KV as a
+ * scheduling lever for under-filled prefill grids ("The FA5090 Optimization
+ * Journey", sec. 2.7, the fourth lever; a loss there because the fp32 round
+ * trip missed L2); here it is a separate entry point that a caller picks,
+ * e.g. with attn_fwd_num_splits.
+ *   Arguments as attn_fwd, plus:
+ *   num_splits: in [1, ceil(Sk/64)].
+ *   workspace : device buffer of at least attn_fwd_split_workspace_bytes(...)
+ *               bytes, owned by the caller; its contents on entry are ignored.
+ * Enqueues the partial kernel, then the combine kernel, on `stream`.
+ */
+int attn_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int Hq, int Hkv, int Sq, int Sk, int d, int causal, float scale,
+                   int dtype, int num_splits, void* workspace, size_t workspace_bytes,
+                   void* stream);
+
+/*
+ * Bytes of device workspace attn_fwd_split needs: fp32 partial outputs
+ * [B,Hq,Sq,num_splits,d] followed (256-byte aligned) by fp32 partial LSEs
+ * [B,Hq,Sq,num_splits].  Returns 0 for invalid arguments.
+ */
+size_t attn_fwd_split_workspace_bytes(int B, int Hq, int Sq, int d, int num_splits);
+
+/*
+ * Recommended num_splits for attn_fwd_split: 1 when attn_fwd's grid (B*Hq
+ * blocks of 256 query rows) already has one workgroup per compute unit (256),
+ * else enough splits to reach that, with at least two 64-key tiles per split.
+ * Returns 1 for invalid arguments.
+ */
+int attn_fwd_num_splits(int B, int Hq, int Sq, int Sk, int d);
 
 /*
  * Bytes of device workspace attn_fwd_decode needs: fp32 partial outputs

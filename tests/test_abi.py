@@ -102,6 +102,55 @@ def test_decode_validation(L, kw, status):
     assert dec(L, **kw) == status
 
 
+def spl(L, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=None, B=1, Hq=2, Hkv=1, Sq=300, Sk=500, d=128, causal=0,
+             scale=0.1, dtype=0, ns=4, ws=P, wsb=1 << 30)
+    a.update(kw)
+    return L.attn_fwd_split(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+                            a["Sq"], a["Sk"], a["d"], a["causal"], a["scale"], a["dtype"], a["ns"],
+                            a["ws"], a["wsb"], None)
+
+
+@cpu_only
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), A.ATTN_ERR_NULL), (dict(B=0), A.ATTN_ERR_SHAPE),
+    (dict(Hq=3, Hkv=2), A.ATTN_ERR_SHAPE), (dict(d=96), A.ATTN_ERR_UNSUPPORTED),
+    (dict(dtype=3), A.ATTN_ERR_UNSUPPORTED), (dict(causal=-1), A.ATTN_ERR_VALUE),
+    (dict(scale=float("nan")), A.ATTN_ERR_VALUE),
+    # 500 keys are 8 tiles of 64: 1..8 splits are valid
+    (dict(ns=0), A.ATTN_ERR_VALUE), (dict(ns=9), A.ATTN_ERR_VALUE), (dict(ns=8), A.ATTN_ERR_NO_DEVICE),
+    (dict(wsb=16), A.ATTN_ERR_WORKSPACE), (dict(ws=None), A.ATTN_ERR_WORKSPACE),
+    (dict(ws=ctypes.c_void_p((1 << 20) + 4)), A.ATTN_ERR_ALIGN),
+    (dict(o=ctypes.c_void_p((1 << 20) + 8)), A.ATTN_ERR_ALIGN),
+    (dict(Sk=1 << 24, ns=4), A.ATTN_ERR_SHAPE), (dict(d=64), A.ATTN_ERR_NO_DEVICE),
+    (dict(causal=1), A.ATTN_ERR_NO_DEVICE), (dict(), A.ATTN_ERR_NO_DEVICE),
+])
+def test_split_validation(L, kw, status):
+    assert spl(L, **kw) == status
+    assert A.last_error() != ""
+
+
+def test_split_workspace_and_recommendation(L):
+    # fp32 partial O [B,Hq,Sq,S,d] then fp32 partial LSE [B,Hq,Sq,S], each 256-byte aligned
+    assert A.attn_fwd_split_workspace_bytes(1, 1, 512, 128, 8) == 512 * 8 * 128 * 4 + 512 * 8 * 4
+    assert A.attn_fwd_split_workspace_bytes(1, 1, 3, 64, 1) == 768 + 256
+    assert A.attn_fwd_split_workspace_bytes(1, 0, 3, 64, 1) == 0
+    # 2 blocks of 256 rows, 8 tiles of keys: 128 splits wanted, two tiles per split -> 4
+    assert A.attn_fwd_num_splits(1, 1, 512, 512, 128) == 4
+    # 1 block, 128 tiles: 256 splits wanted -> 64 (two tiles each)
+    assert A.attn_fwd_num_splits(1, 1, 100, 8192, 128) == 64
+    # 16 blocks, 32 tiles: 16 splits wanted, 16 allowed
+    assert A.attn_fwd_num_splits(1, 2, 2048, 2048, 128) == 16
+    # a single tile cannot be split
+    assert A.attn_fwd_num_splits(1, 1, 64, 64, 128) == 1
+    assert A.attn_fwd_num_splits(1, 1, 64, 100, 128) == 1
+    # already 256 items or more: no split
+    assert A.attn_fwd_num_splits(4, 16, 1024, 1024, 128) == 1
+    assert A.attn_fwd_num_splits(2, 16, 2048, 2048, 64) == 1
+    assert A.attn_fwd_num_splits(1, 16, 2048, 2048, 64) == 2
+    assert A.attn_fwd_num_splits(0, 16, 2048, 2048, 64) == 1
+
+
 @cpu_only
 def test_combine_validation(L):
     assert L.attn_splitkv_combine(P, P, P, None, 1, 1, 128, 0, 0, None) == A.ATTN_ERR_VALUE
