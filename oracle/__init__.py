@@ -18,6 +18,9 @@ computes, with the passages it follows, is stated in ``oracle.h``:
   correctness gate, "The FA5090 Optimization Journey", sec. 2.1).
 * ``split_partials`` / ``combine``: the split-KV decode partials and their
   log-sum-exp merge.
+* ``decode_e4m3`` / ``round_e4m3`` / ``attention_fp8``: the OCP E4M3 format
+  and attention over per-tensor-scaled E4M3 inputs, with its FP8 reference
+  (unnormalised weights rounded to E4M3 before the product with V).
 """
 from __future__ import annotations
 
@@ -64,8 +67,14 @@ def _load():
     lib.oracle_split_partials.argtypes = [c_u16p, c_u16p, c_u16p, i, i, i, i, i, i, dbl, i,
                                           c_dp, c_dp]
     lib.oracle_combine.argtypes = [c_dp, c_dp, i64, i, i, c_dp, c_dp]
+    c_u8p = ctypes.POINTER(ctypes.c_uint8)
+    lib.oracle_decode_e4m3.argtypes = [c_u8p, i64, c_dp]
+    lib.oracle_round_e4m3.argtypes = [c_dp, i64, c_u8p]
+    lib.oracle_attention_fp8_rows.argtypes = [c_u8p, c_u8p, c_u8p, i, i, i, i, i, i, i, dbl, dbl,
+                                              dbl, dbl, i, c_i64p, i64, c_dp, c_dp, c_dp, i]
     for fn in (lib.oracle_decode, lib.oracle_round, lib.oracle_attention_rows,
-               lib.oracle_split_partials, lib.oracle_combine):
+               lib.oracle_split_partials, lib.oracle_combine, lib.oracle_decode_e4m3,
+               lib.oracle_round_e4m3, lib.oracle_attention_fp8_rows):
         fn.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -173,3 +182,65 @@ def combine(o_part, lse_part):
                                 R, d, ns, _ptr(o, ctypes.c_double), _ptr(lse, ctypes.c_double))
     _check(rc, "combine")
     return o, lse
+
+
+def _u8(a):
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.uint8:
+        raise TypeError("FP8 inputs are 8-bit patterns (numpy uint8), got %s" % a.dtype)
+    return a
+
+
+def decode_e4m3(bits) -> np.ndarray:
+    """E4M3 (OCP, no infinities) patterns -> float64 values (exact)."""
+    bits = _u8(bits)
+    out = np.empty(bits.shape, dtype=np.float64)
+    _check(_load().oracle_decode_e4m3(_ptr(bits, ctypes.c_uint8), bits.size,
+                                      _ptr(out, ctypes.c_double)), "decode_e4m3")
+    return out
+
+
+def round_e4m3(values) -> np.ndarray:
+    """float64 -> E4M3 patterns, nearest-even, saturating at 448."""
+    values = np.ascontiguousarray(values, dtype=np.float64)
+    out = np.empty(values.shape, dtype=np.uint8)
+    _check(_load().oracle_round_e4m3(_ptr(values, ctypes.c_double), values.size,
+                                     _ptr(out, ctypes.c_uint8)), "round_e4m3")
+    return out
+
+
+def attention_fp8_rows(q, k, v, causal: bool, scale: float, q_descale: float, k_descale: float,
+                       v_descale: float, out_dtype: int, rows, want_ref: bool = True,
+                       nthreads: int = 0):
+    """FP8 oracle rows.  q [B,Hq,Sq,d], k/v [B,Hkv,Sk,d] as uint8 E4M3 patterns; the
+    real inputs are the decoded values times the per-tensor descales.  Returns
+    (o [n,d], lse [n], o_ref [n,d] or None), float64; o_ref is the FP8
+    reference (unnormalised weights rounded to E4M3, O rounded to out_dtype)."""
+    q, k, v = _u8(q), _u8(k), _u8(v)
+    B, Hq, Sq, d = q.shape
+    Bk, Hkv, Sk, dk = k.shape
+    if Bk != B or dk != d or v.shape != k.shape:
+        raise ValueError("shape mismatch")
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    n = rows.size
+    o = np.empty((n, d), dtype=np.float64)
+    lse = np.empty(n, dtype=np.float64)
+    o_ref = np.empty((n, d), dtype=np.float64) if want_ref else None
+    rc = _load().oracle_attention_fp8_rows(
+        _ptr(q, ctypes.c_uint8), _ptr(k, ctypes.c_uint8), _ptr(v, ctypes.c_uint8), B, Hq, Hkv, Sq,
+        Sk, d, 1 if causal else 0, float(scale), float(q_descale), float(k_descale),
+        float(v_descale), out_dtype, _ptr(rows, ctypes.c_int64), n, _ptr(o, ctypes.c_double),
+        _ptr(lse, ctypes.c_double), _ptr(o_ref, ctypes.c_double) if want_ref else None, nthreads)
+    _check(rc, "attention_fp8_rows")
+    return o, lse, o_ref
+
+
+def attention_fp8(q, k, v, causal: bool, scale: float, q_descale: float, k_descale: float,
+                  v_descale: float, out_dtype: int, want_ref: bool = True, nthreads: int = 0):
+    """All rows of the FP8 oracle: (o [B,Hq,Sq,d], lse [B,Hq,Sq], o_ref or None)."""
+    B, Hq, Sq, d = q.shape
+    rows = np.arange(B * Hq * Sq, dtype=np.int64)
+    o, lse, o_ref = attention_fp8_rows(q, k, v, causal, scale, q_descale, k_descale, v_descale,
+                                       out_dtype, rows, want_ref, nthreads)
+    shp = (B, Hq, Sq, d)
+    return o.reshape(shp), lse.reshape(B, Hq, Sq), (o_ref.reshape(shp) if want_ref else None)

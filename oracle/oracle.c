@@ -143,6 +143,144 @@ static void attend_row(const double* qrow, const double* kh, const double* vh, i
     for (int c = 0; c < d; ++c) o_ref[c] = decode1(round1(o_ref[c], f), f);
 }
 
+/* ---- OCP 8-bit E4M3 (the "FN" variant: no infinities), from the format's
+ * definition: 1 sign, 4 exponent bits (bias 7), 3 fraction bits; exponent
+ * field 0 holds subnormals m * 2^-9; S.1111.111 is NaN, so the largest finite
+ * magnitude is S.1111.110 = 1.75 * 2^8 = 448. ---- */
+static double decode_e4m3(uint8_t b) {
+  int sign = (b >> 7) & 1;
+  int e = (b >> 3) & 15;
+  int m = b & 7;
+  double v;
+  if (e == 15 && m == 7)
+    v = NAN;
+  else if (e == 0)
+    v = ldexp((double)m, -9);
+  else
+    v = ldexp((double)(8 + m), e - 7 - 3);
+  return sign ? -v : v;
+}
+
+/* Round to E4M3 with round-to-nearest, ties to even; magnitudes past 448
+ * saturate to 448 (the format has no infinity); NaN stays NaN. */
+static uint8_t round_e4m3(double x) {
+  uint8_t sign = signbit(x) ? 0x80u : 0u;
+  if (isnan(x)) return (uint8_t)(sign | 0x7Fu);
+  double a = fabs(x);
+  if (a == 0.0) return sign;
+  if (a >= 448.0) return (uint8_t)(sign | 0x7Eu);
+  int ex;
+  frexp(a, &ex);
+  int e = ex - 1;                     /* a in [2^e, 2^(e+1)) */
+  int qexp = (e < -6 ? -6 : e) - 3;   /* quantum: 2^-9 for subnormals, 2^(e-3) else */
+  double q = ldexp(a, -qexp);
+  double fl = floor(q);
+  double rem = q - fl;
+  double r = fl;
+  if (rem > 0.5 || (rem == 0.5 && fmod(fl, 2.0) != 0.0)) r = fl + 1.0;
+  /* the value is r * 2^qexp; re-encode it (a carry may reach the next binade) */
+  double y = ldexp(r, qexp);
+  if (y >= 448.0) return (uint8_t)(sign | 0x7Eu);
+  if (y < ldexp(1.0, -6)) return (uint8_t)(sign | (uint8_t)r); /* subnormal: m = r */
+  frexp(y, &ex);
+  e = ex - 1;
+  int m = (int)(ldexp(y, 3 - e)) - 8;
+  return (uint8_t)(sign | ((e + 7) << 3) | m);
+}
+
+int oracle_decode_e4m3(const uint8_t* in, int64_t n, double* out) {
+  if (n < 0 || (n && (!in || !out))) return -1;
+  for (int64_t i = 0; i < n; ++i) out[i] = decode_e4m3(in[i]);
+  return 0;
+}
+
+int oracle_round_e4m3(const double* in, int64_t n, uint8_t* out) {
+  if (n < 0 || (n && (!in || !out))) return -1;
+  for (int64_t i = 0; i < n; ++i) out[i] = round_e4m3(in[i]);
+  return 0;
+}
+
+static int check_shapes(int B, int Hq, int Hkv, int Sq, int Sk, int d);
+
+int oracle_attention_fp8_rows(const uint8_t* q, const uint8_t* k, const uint8_t* v, int B, int Hq,
+                              int Hkv, int Sq, int Sk, int d, int causal, double scale,
+                              double q_descale, double k_descale, double v_descale, int out_dtype,
+                              const int64_t* rows, int64_t n_rows, double* o, double* lse,
+                              double* o_ref, int nthreads) {
+  if (out_dtype < 0 || out_dtype > 1 || check_shapes(B, Hq, Hkv, Sq, Sk, d)) return -1;
+  if (!q || !k || !v || !rows || !o || !lse || n_rows < 0) return -1;
+  const int64_t total_rows = (int64_t)B * Hq * Sq;
+  for (int64_t r = 0; r < n_rows; ++r)
+    if (rows[r] < 0 || rows[r] >= total_rows) return -2;
+  const fmt16* f = &FMT[out_dtype];
+  const int group = Hq / Hkv;
+  /* the real inputs are q8 * q_descale etc.; the descales of q and k only
+   * scale the scores, v's scales the output */
+  const double s_scale = scale * q_descale * k_descale;
+  int err = 0;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+  (void)nthreads;
+#endif
+#pragma omp parallel
+  {
+    double* s = (double*)malloc(sizeof(double) * (size_t)Sk);
+    double* qd = (double*)malloc(sizeof(double) * (size_t)d);
+    double* kd = (double*)malloc(sizeof(double) * (size_t)Sk * d);
+    double* vd = (double*)malloc(sizeof(double) * (size_t)Sk * d);
+    int64_t cached_head = -1;
+    if (!s || !qd || !kd || !vd) {
+#pragma omp atomic write
+      err = -3;
+    }
+#pragma omp for schedule(dynamic, 4)
+    for (int64_t r = 0; r < n_rows; ++r) {
+      if (err) continue;
+      int64_t row = rows[r];
+      int i = (int)(row % Sq);
+      int64_t bh = row / Sq;
+      int hq = (int)(bh % Hq);
+      int b = (int)(bh / Hq);
+      int64_t kv_head = (int64_t)b * Hkv + hq / group;
+      if (kv_head != cached_head) {
+        const uint8_t* kh = k + kv_head * Sk * d;
+        const uint8_t* vh = v + kv_head * Sk * d;
+        for (int64_t e = 0; e < (int64_t)Sk * d; ++e) {
+          kd[e] = decode_e4m3(kh[e]);
+          vd[e] = v_descale * decode_e4m3(vh[e]);
+        }
+        cached_head = kv_head;
+      }
+      const uint8_t* qr = q + row * d;
+      for (int c = 0; c < d; ++c) qd[c] = decode_e4m3(qr[c]);
+      int64_t last = causal ? (int64_t)i + (Sk - Sq) : (int64_t)Sk - 1;
+      int nvis = last < 0 ? 0 : (last >= Sk ? Sk : (int)(last + 1));
+      double* orow = o + r * d;
+      attend_row(qd, kd, vd, Sk, d, nvis, s_scale, s, orow, lse + r, NULL, f);
+      if (o_ref) {
+        /* s[0 .. nvis) now holds the weights exp(s_j - m) against the row max */
+        double* oref = o_ref + r * d;
+        double l = 0.0;
+        for (int c = 0; c < d; ++c) oref[c] = 0.0;
+        for (int j = 0; j < nvis; ++j) {
+          l += s[j];
+          double pr = decode_e4m3(round_e4m3(s[j]));
+          const double* vr = vd + (int64_t)j * d;
+          for (int c = 0; c < d; ++c) oref[c] += pr * vr[c];
+        }
+        for (int c = 0; c < d; ++c)
+          oref[c] = nvis > 0 ? decode1(round1(oref[c] / l, f), f) : 0.0;
+      }
+    }
+    free(s);
+    free(qd);
+    free(kd);
+    free(vd);
+  }
+  return err;
+}
+
 static int check_shapes(int B, int Hq, int Hkv, int Sq, int Sk, int d) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Sq <= 0 || Sk <= 0 || d <= 0) return -1;
   if (Hq % Hkv != 0) return -1;

@@ -71,6 +71,33 @@ int oracle_split_partials(const uint16_t* q, const uint16_t* k, const uint16_t* 
 int oracle_combine(const double* o_part, const double* lse_part, int64_t R, int d, int num_splits,
                    double* o, double* lse);
 
+/*
+ * OCP 8-bit floating point, E4M3 with no infinities ("E4M3FN"; the OCP 8-bit
+ * Floating Point Specification, OFP8): 1 sign, 4 exponent bits (bias 7),
+ * 3 fraction bits; subnormals m * 2^-9; S.1111.111 is NaN; largest finite
+ * magnitude 448.  Decode is exact; rounding is to nearest, ties to even, with
+ * magnitudes beyond 448 saturated to 448.
+ */
+int oracle_decode_e4m3(const uint8_t* in, int64_t n, double* out);
+int oracle_round_e4m3(const double* in, int64_t n, uint8_t* out);
+
+/*
+ * FP8 attention.  q, k, v hold E4M3 patterns; the real inputs are
+ * q8 * q_descale, k8 * k_descale and v8 * v_descale (per-tensor scales).  o
+ * and lse are the plain definition above on those real values.
+ * o_ref (may be NULL) is the FP8 reference: the unnormalised weights
+ * exp(s_j - m) (m the exact row max, so each is in (0, 1]) are rounded to
+ * E4M3 before the product with V, the sum of the unrounded weights
+ * normalises, and O is rounded to out_dtype (0 = binary16, 1 = bfloat16).
+ * An FP8 kernel can only round the weights it feeds to the matrix unit, which
+ * are unnormalised; the normalisation follows in fp32.
+ */
+int oracle_attention_fp8_rows(const uint8_t* q, const uint8_t* k, const uint8_t* v, int B, int Hq,
+                              int Hkv, int Sq, int Sk, int d, int causal, double scale,
+                              double q_descale, double k_descale, double v_descale, int out_dtype,
+                              const int64_t* rows, int64_t n_rows, double* o, double* lse,
+                              double* o_ref, int nthreads);
+
 #ifdef __cplusplus
 }
 #endif
