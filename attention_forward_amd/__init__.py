@@ -31,7 +31,7 @@ ATTN_ERR_VALUE = 8
 ATTN_F16 = 0
 ATTN_BF16 = 1
 
-EXPORTED = ("attn_fwd", "attn_fwd_split", "attn_fwd_split_workspace_bytes", "attn_fwd_num_splits",
+EXPORTED = ("attn_fwd", "attn_fwd_fp8", "attn_fwd_split", "attn_fwd_split_workspace_bytes", "attn_fwd_num_splits",
             "attn_decode_workspace_bytes", "attn_fwd_decode", "attn_splitkv_combine",
             "attn_last_error")
 
@@ -56,6 +56,8 @@ def lib() -> ctypes.CDLL:
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     L.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp]
     L.attn_fwd.restype = i
+    L.attn_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, f, f, f, i, vp]
+    L.attn_fwd_fp8.restype = i
     L.attn_fwd_split.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, i, vp, sz, vp]
     L.attn_fwd_split.restype = i
     L.attn_fwd_split_workspace_bytes.argtypes = [i, i, i, i, i]
@@ -137,6 +139,40 @@ def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
     st = lib().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Sq, Sk, d,
                         1 if causal else 0, float(scale), _dtype_code(q), _stream(q.device))
+    _check(st)
+    return out, lse
+
+
+def attn_fwd_fp8(q, k, v, causal: bool = False, scale: float | None = None,
+                 q_descale: float = 1.0, k_descale: float = 1.0, v_descale: float = 1.0,
+                 out_dtype=None, out=None, lse=None, want_lse: bool = True):
+    """FP8 prefill: q [B,Hq,Sq,128], k and v [B,Hkv,Sk,128] contiguous E4M3 device
+    tensors (torch.float8_e4m3fn or uint8 bytes) holding the inputs divided by
+    their per-tensor descales.  Returns (o in out_dtype (bf16 default), lse fp32)."""
+    import torch
+
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _require(t, nm)
+        if t.element_size() != 1:
+            raise AttnError(ATTN_ERR_UNSUPPORTED, "%s must hold 1-byte E4M3 values" % nm)
+    B, Hq, Sq, d = q.shape
+    Bk, Hkv, Sk, dk = k.shape
+    if Bk != B or dk != d or tuple(v.shape) != tuple(k.shape):
+        raise AttnError(ATTN_ERR_SHAPE, "q %s / k %s / v %s shapes disagree"
+                        % (tuple(q.shape), tuple(k.shape), tuple(v.shape)))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out_dtype is None:
+        out_dtype = out.dtype if out is not None else torch.bfloat16
+    code = ATTN_F16 if out_dtype == torch.float16 else ATTN_BF16 if out_dtype == torch.bfloat16 \
+        else -1
+    if out is None:
+        out = torch.empty((B, Hq, Sq, d), dtype=out_dtype, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    st = lib().attn_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Sq, Sk,
+                            d, 1 if causal else 0, float(scale), float(q_descale),
+                            float(k_descale), float(v_descale), code, _stream(q.device))
     _check(st)
     return out, lse
 

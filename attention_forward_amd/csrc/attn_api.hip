@@ -86,6 +86,47 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
   return hip_status(attn::launch_fwd(a, static_cast<hipStream_t>(stream)), "attn_fwd launch");
 }
 
+int attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+                 int Hkv, int Sq, int Sk, int d, int causal, float scale, float q_descale,
+                 float k_descale, float v_descale, int out_dtype, void* stream) {
+  g_err[0] = '\0';
+  if (!q || !k || !v || !o) return fail(ATTN_ERR_NULL, "attn_fwd_fp8: q, k, v and o must be non-NULL");
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Sq <= 0 || Sk <= 0 || d <= 0)
+    return fail(ATTN_ERR_SHAPE,
+                "attn_fwd_fp8: sizes must be positive (B=%d Hq=%d Hkv=%d Sq=%d Sk=%d d=%d)", B, Hq,
+                Hkv, Sq, Sk, d);
+  if (Hq % Hkv != 0)
+    return fail(ATTN_ERR_SHAPE, "attn_fwd_fp8: Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  if (out_dtype != ATTN_F16 && out_dtype != ATTN_BF16)
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd_fp8: output dtype %d is not 0 (fp16) or 1 (bf16)",
+                out_dtype);
+  if (d != 128)
+    return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd_fp8: head dim %d (128 is implemented)", d);
+  if (causal != 0 && causal != 1) return fail(ATTN_ERR_VALUE, "attn_fwd_fp8: causal must be 0 or 1");
+  const double folded = (double)scale * q_descale * k_descale;
+  if (!std::isfinite(scale) || scale < 0.0f || !std::isfinite(q_descale) || q_descale <= 0.0f ||
+      !std::isfinite(k_descale) || k_descale <= 0.0f || !std::isfinite(v_descale) ||
+      v_descale <= 0.0f || !std::isfinite(folded * 1.4426950408889634074) ||
+      !std::isfinite((float)(folded * 1.4426950408889634074)))
+    return fail(ATTN_ERR_VALUE,
+                "attn_fwd_fp8: scale must be finite and >= 0, descales finite and > 0");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+      (lse && !aligned4(lse)))
+    return fail(ATTN_ERR_ALIGN, "attn_fwd_fp8: q, k, v, o must be 16-byte aligned, lse 4-byte");
+  const long long items = (long long)B * Hq * ((Sq + attn::FWD_BR - 1) / attn::FWD_BR);
+  const long long q_elems = (long long)B * Hq * Sq * d;
+  const long long kv_elems = (long long)B * Hkv * Sk * d;
+  if (items > INT_MAX || q_elems > (1LL << 46) || kv_elems > (1LL << 46))
+    return fail(ATTN_ERR_SHAPE, "attn_fwd_fp8: problem too large for one launch");
+  if (Sq > kMaxSeq || Sk > kMaxSeq)
+    return fail(ATTN_ERR_SHAPE, "attn_fwd_fp8: sequence length above %d", kMaxSeq);
+  int st = check_device();
+  if (st != ATTN_OK) return st;
+  attn::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, d, causal,
+                  (float)(folded * 1.4426950408889634074), out_dtype, v_descale, 1};
+  return hip_status(attn::launch_fwd(a, static_cast<hipStream_t>(stream)), "attn_fwd_fp8 launch");
+}
+
 int attn_fwd_num_splits(int B, int Hq, int Sq, int Sk, int d) {
   if (B <= 0 || Hq <= 0 || Sq <= 0 || Sk <= 0 || !attn::head_dim_supported(d)) return 1;
   const long long items = (long long)B * Hq * ((Sq + attn::FWD_BR - 1) / attn::FWD_BR);

@@ -46,6 +46,7 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((__vector_size__(8)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -246,6 +247,134 @@ __device__ __forceinline__ LaneAddr lane_addresses() {
   return a;
 }
 
+// ---- FP8 (OCP E4M3) operands at head dimension 128 ----
+// A row is 128 bytes, so tiles, loads and the K reads are those of the 16-bit
+// layout at head dimension 64 (Geom<64>).  Both matrix products use
+// v_mfma_scale_f32_32x32x64_f8f6f4 with unit block scales: a lane holds 32
+// bytes of each operand, and A and B use the same byte -> k order, so any
+// consistent assignment of the 64 k values to (lane half, byte) is exact.
+//
+// V is read with the byte-transposing read ds_read_b64_tr_b8: in each 16-lane
+// group, lane 8u + i receives byte i of the 8 bytes addressed by lanes u, 2+u,
+// ..., 14+u, one from each.  So a group's lanes address 8 keys (rows) at two
+// 8-byte column offsets, and each destination lane ends up with one column
+// (one d) of 8 keys.  XOR of the 16-byte slot with 2 * (row bit 1) + 4 * (row
+// bit 3) puts the 8 rows of a 32-lane pass on distinct banks.
+__device__ __forceinline__ int v_swz8(int row) {
+  return (((row >> 1) & 1) << 1) | (((row >> 3) & 1) << 2);
+}
+
+template <bool IS_V>
+__device__ __forceinline__ unsigned load_lane_offset8(int chunk) {
+  using G = Geom<64>;
+  const int lane = threadIdx.x & 63;
+  const int r = chunk * G::RPC + lane / G::SLOTS;
+  const int slot = (lane % G::SLOTS) ^ (IS_V ? v_swz8(r) : k_swz<64>(r));
+  return (unsigned)(r * G::ROW + slot * 16);
+}
+
+// k[st]: K operand half st (16-byte slot 2st + g of row n), as at d = 64 in 16
+// bits; the FP8 k-step st8 uses halves 2st8 and 2st8 + 1.  v[db]: the byte
+// address this lane supplies to the transposing reads of d-block db: key row
+// 8(x>>3) + 4(h>>1) + ((x>>1)&3) (+16 per read), column 32db + 16(h&1) +
+// 8(x&1), with h = lane>>4, x = lane&15.  The keys so read for destination
+// lane half g are 16t + 8(e>>2) + 4g + (e&3), e = 0..7, in read t: exactly the
+// keys whose scores the lane holds in accumulator elements 8t' + e of key
+// block t>>1 (t' = t&1), in the order store_p packs them.
+__device__ __forceinline__ LaneAddr lane_addresses8() {
+  LaneAddr a = lane_addresses<64>();
+  const int lane = threadIdx.x & 63;
+  const int h = lane >> 4, x = lane & 15;
+  const int row = 8 * (x >> 3) + 4 * (h >> 1) + ((x >> 1) & 3);
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+    const int slot = 2 * db + (h & 1);
+    a.v[db] = (unsigned)(row * 128 + ((slot ^ v_swz8(row)) * 16) + 8 * (x & 1));
+  }
+  return a;
+}
+
+__device__ __forceinline__ f32x16 mfma8(const u32x8& a, const u32x8& b, f32x16 c) {
+  typedef int i32x8 __attribute__((ext_vector_type(8)));
+  // format 0 (E4M3) for both operands, block scales 2^(127 - 127) = 1
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(__builtin_bit_cast(i32x8, a),
+                                                         __builtin_bit_cast(i32x8, b), c, 0, 0,
+                                                         0, 127, 0, 127);
+}
+
+template <int OFF>
+__device__ __forceinline__ u32x2 lds_tr8(unsigned addr) {
+  u32x2 r;
+  asm volatile("ds_read_b64_tr_b8 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
+  return r;
+}
+template <int N>
+__device__ __forceinline__ void lgkm_wait8(u32x8& x) {
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(x) : "n"(N));
+}
+
+// S^T = K Q^T in FP8: 2 key blocks x 2 k-steps of 64 d; all eight K reads are
+// issued first, each operand waited for just before its MFMA.
+template <int QB>
+__device__ __forceinline__ void qk_step8(unsigned kbase, const LaneAddr& la,
+                                         const u32x8 (&qf)[QB][2], f32x16 (&s)[2][QB]) {
+  u32x8 ko[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int kb = i >> 1, st = i & 1;
+    u32x4 lo, hi;
+    if (kb == 0) {
+      lo = lds_b128<0>(kbase + la.k[2 * st]);
+      hi = lds_b128<0>(kbase + la.k[2 * st + 1]);
+    } else {
+      lo = lds_b128<32 * 128>(kbase + la.k[2 * st]);
+      hi = lds_b128<32 * 128>(kbase + la.k[2 * st + 1]);
+    }
+    ko[i] = u32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    switch (i) {
+      case 0: lgkm_wait8<6>(ko[0]); break;
+      case 1: lgkm_wait8<4>(ko[1]); break;
+      case 2: lgkm_wait8<2>(ko[2]); break;
+      default: lgkm_wait8<0>(ko[3]); break;
+    }
+    const int kb = i >> 1, st = i & 1;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+      s[kb][qb] = mfma8(ko[i], qf[qb][st], st == 0 ? f32x16{} : s[kb][qb]);
+  }
+}
+
+// O^T += V^T P^T in FP8: 4 d-blocks, one MFMA of all 64 keys each; an operand
+// is four transposing reads (keys 16t .. 16t+15 of the lane half), two
+// operands in flight.
+template <int QB>
+__device__ __forceinline__ void pv_step8(unsigned vbase, const LaneAddr& la,
+                                         const u32x8 (&pf)[QB], f32x16 (&o)[4][QB]) {
+  u32x8 vo[2];
+  auto read_v = [&](int db, u32x8& dst) {
+    const unsigned a = vbase + la.v[db];
+    const u32x2 r0 = lds_tr8<0>(a), r1 = lds_tr8<16 * 128>(a), r2 = lds_tr8<32 * 128>(a),
+                r3 = lds_tr8<48 * 128>(a);
+    dst = u32x8{r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
+  };
+  read_v(0, vo[0]);
+  read_v(1, vo[1]);
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+    u32x8& cur = vo[db & 1];
+    if (db < 3)
+      lgkm_wait8<4>(cur);
+    else
+      lgkm_wait8<0>(cur);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) o[db][qb] = mfma8(cur, pf[qb], o[db][qb]);
+    if (db + 2 < 4) read_v(db + 2, vo[db & 1]);
+  }
+}
+
 // ---- the three parts of one 64-key tile, for QB blocks of 32 queries ----
 //
 // qf: Q^T operands [QB][DSTEPS] (16-deep d steps).  s: S^T accumulators [2 key
@@ -309,6 +438,31 @@ __device__ __forceinline__ void qk_step(unsigned kbase, const LaneAddr& la,
   }
 }
 
+// The P^T operand of one tile, written eight weights at a time: w[0..7] are
+// the weights of accumulator elements 8t .. 8t+7 of key block kb.
+// 16-bit MFMA: pf[kb][t][qb] holds them rounded to the dtype, two per register.
+template <int DT, int QB>
+__device__ __forceinline__ void store_p(u32x4 (&pf)[2][2][QB], int kb, int t, int qb,
+                                        const float (&w)[8]) {
+  u32x4 x;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) x[e] = pack2<DT>(w[2 * e], w[2 * e + 1]);
+  pf[kb][t][qb] = x;
+}
+// FP8 MFMA: pf[qb] holds all 32 weights of the tile as E4M3 bytes, byte
+// 16kb + 8t + e for element 8t + e of key block kb (round to nearest even;
+// the weights are at most 2^8, inside the format's range).
+template <int DT, int QB>
+__device__ __forceinline__ void store_p(u32x8 (&pf)[QB], int kb, int t, int qb,
+                                        const float (&w)[8]) {
+  int lo = __builtin_amdgcn_cvt_pk_fp8_f32(w[0], w[1], 0, false);
+  lo = __builtin_amdgcn_cvt_pk_fp8_f32(w[2], w[3], lo, true);
+  int hi = __builtin_amdgcn_cvt_pk_fp8_f32(w[4], w[5], 0, false);
+  hi = __builtin_amdgcn_cvt_pk_fp8_f32(w[6], w[7], hi, true);
+  pf[qb][4 * kb + 2 * t] = (unsigned)lo;
+  pf[qb][4 * kb + 2 * t + 1] = (unsigned)hi;
+}
+
 // Online softmax of one S^T tile: scores -> P^T operands pf (rounded to the
 // dtype), rescaled O and updated m, l.  MASK: apply the key-validity and
 // causal test per score (tiles that cross the diagonal or the end of the keys
@@ -327,10 +481,10 @@ __device__ __forceinline__ void qk_step(unsigned kbase, const LaneAddr& la,
 // which O must be multiplied by alpha: a row whose max was -inf has O = 0).
 // The caller then applies alpha itself; until that happens alpha is exactly 1
 // for every lane, so skipping the multiply changes no bit.
-template <int DT, int QB, bool MASK, bool RESCALE_O = true, int NDB = 4>
+template <int DT, int QB, bool MASK, bool RESCALE_O = true, int NDB = 4, typename PF>
 __device__ __forceinline__ bool softmax_step(f32x16 (&s)[2][QB], f32x16 (&o)[NDB][QB],
                                              float (&m)[QB], float (&l)[QB],
-                                             u32x4 (&pf)[2][2][QB], float scale_log2, int key0,
+                                             PF& pf, float scale_log2, int key0,
                                              int qrow0, int n_keys, bool causal, int causal_off,
                                              float (&alpha_out)[QB]) {
   bool moved = false;
@@ -391,16 +545,15 @@ __device__ __forceinline__ bool softmax_step(f32x16 (&s)[2][QB], f32x16 (&o)[NDB
         rs += p;
       }
     l[qb] = rs;
-    // P rounded to the dtype (RNE) for the MFMA
+    // P rounded to the MFMA's input format (RNE)
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        u32x4 w;
+        float w[8];
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          w[e] = pack2<DT>(s[kb][qb][8 * t + 2 * e], s[kb][qb][8 * t + 2 * e + 1]);
-        pf[kb][t][qb] = w;
+        for (int e = 0; e < 8; ++e) w[e] = s[kb][qb][8 * t + e];
+        store_p<DT, QB>(pf, kb, t, qb, w);
       }
   }
   if constexpr (RESCALE_O)
@@ -424,10 +577,9 @@ __device__ __forceinline__ bool softmax_step(f32x16 (&s)[2][QB], f32x16 (&o)[NDB
 // An infinite or NaN sum fails the test as well.  ("The FA5090 Optimization
 // Journey", sec. 3, threshold rescale; the bound on the weights is what keeps
 // the fp32 sums and the rounded P in range.)
-template <int DT, int QB>
+template <int DT, int QB, typename PF>
 __device__ __forceinline__ bool softmax_fast(const f32x16 (&s)[2][QB], const float (&m)[QB],
-                                             float (&l)[QB], u32x4 (&pf)[2][2][QB],
-                                             float scale_log2) {
+                                             float (&l)[QB], PF& pf, float scale_log2) {
   constexpr float BOUND = 128.0f;  // 2^(TAU - 1) with TAU = 8
   bool bad = false;
   float rs_q[QB];
@@ -439,18 +591,13 @@ __device__ __forceinline__ bool softmax_fast(const f32x16 (&s)[2][QB], const flo
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        u32x4 w;
+        float w[8];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p0 =
-              __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][qb][8 * t + 2 * e], scale_log2, neg_m));
-          const float p1 = __builtin_amdgcn_exp2f(
-              __builtin_fmaf(s[kb][qb][8 * t + 2 * e + 1], scale_log2, neg_m));
-          rs += p0;
-          rs += p1;
-          w[e] = pack2<DT>(p0, p1);
+        for (int e = 0; e < 8; ++e) {
+          w[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][qb][8 * t + e], scale_log2, neg_m));
+          rs += w[e];
         }
-        pf[kb][t][qb] = w;
+        store_p<DT, QB>(pf, kb, t, qb, w);
       }
     bad |= !(rs < l[qb] + BOUND);
     rs_q[qb] = rs;

@@ -30,6 +30,72 @@ namespace attn {
 
 static_assert(KT == FWD_KT, "the host's split arithmetic uses the kernels' tile");
 
+// Input formats.  In16<DT, HD>: fp16 (DT 0) or bf16 (DT 1) Q, K, V at head
+// dimension HD, O in the same dtype.  In8<DT>: OCP E4M3 Q, K, V at head
+// dimension 128 with per-tensor descales (Q's and K's folded into the score
+// scale on the host, V's applied to O), O in dtype DT.  Each gives the LDS
+// layout (Geom of the row size in bytes), the operand fragments and the two
+// matrix steps of a tile; the schedule around them is the same.
+template <int DT_, int HD_>
+struct In16 {
+  static constexpr int DT = DT_, HD = HD_, LAYOUT_HD = HD_, DBLOCKS = HD_ / 32;
+  static constexpr bool FP8 = false;
+  using QFrag = u32x4[1][Geom<HD_>::DSTEPS];
+  using PFrag = u32x4[2][2][1];
+  __device__ static LaneAddr lanes() { return lane_addresses<HD_>(); }
+  template <bool IS_V>
+  __device__ static unsigned load_offset(int chunk) {
+    return load_lane_offset<HD_, IS_V>(chunk);
+  }
+  // lane holds Q[row][16*st + 8*g .. +7] for its query; row_off: the row's first byte
+  __device__ static void load_q(QFrag& qf, __amdgpu_buffer_rsrc_t qr, unsigned row_off) {
+    const int g = (threadIdx.x >> 5) & 1;
+#pragma unroll
+    for (int st = 0; st < Geom<HD_>::DSTEPS; ++st)
+      qf[0][st] = load_b128(qr, row_off + 16 * g + 32 * st);
+  }
+  __device__ static void qk(unsigned kbase, const LaneAddr& la, const QFrag& qf,
+                            f32x16 (&s)[2][1]) {
+    qk_step<DT_, 1, HD_>(kbase, la, qf, s);
+  }
+  __device__ static void pv(unsigned vbase, const LaneAddr& la, const PFrag& pf,
+                            f32x16 (&o)[DBLOCKS][1]) {
+    pv_step<DT_, 1, HD_>(vbase, la, pf, o);
+  }
+};
+
+template <int DT_>
+struct In8 {
+  static constexpr int DT = DT_, HD = 128, LAYOUT_HD = 64, DBLOCKS = 4;
+  static constexpr bool FP8 = true;
+  using QFrag = u32x8[1][2];
+  using PFrag = u32x8[1];
+  __device__ static LaneAddr lanes() { return lane_addresses8(); }
+  template <bool IS_V>
+  __device__ static unsigned load_offset(int chunk) {
+    return load_lane_offset8<IS_V>(chunk);
+  }
+  // lane holds Q[row] bytes of slots 4st + g and 4st + 2 + g for k-step st,
+  // the halves qk_step8 reads of K
+  __device__ static void load_q(QFrag& qf, __amdgpu_buffer_rsrc_t qr, unsigned row_off) {
+    const int g = (threadIdx.x >> 5) & 1;
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const u32x4 lo = load_b128(qr, row_off + 16 * (4 * st + g));
+      const u32x4 hi = load_b128(qr, row_off + 16 * (4 * st + 2 + g));
+      qf[0][st] = u32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+  }
+  __device__ static void qk(unsigned kbase, const LaneAddr& la, const QFrag& qf,
+                            f32x16 (&s)[2][1]) {
+    qk_step8<1>(kbase, la, qf, s);
+  }
+  __device__ static void pv(unsigned vbase, const LaneAddr& la, const PFrag& pf,
+                            f32x16 (&o)[DBLOCKS][1]) {
+    pv_step8<1>(vbase, la, pf, o);
+  }
+};
+
 // PART: split-KV form for grids too small to fill the chip.  Work item
 // (q block, batch*head, split s) attends to keys [s * split_keys, (s + 1) *
 // split_keys) only and writes the normalised partial O in fp32 and its LSE
@@ -38,18 +104,21 @@ static_assert(KT == FWD_KT, "the host's split arithmetic uses the kernels' tile"
 // it sees K and V from the split's first key on, Sk cut to the split and the
 // causal offset shifted by the split's start.  A split with no visible key
 // writes O = 0 and LSE = -inf, which the combine weighs by 0.
-template <int DT, int HD, bool PART>
+// o_scale multiplies O before it is rounded (V's descale in FP8, else 1).
+template <typename F, bool PART>
 __global__ __launch_bounds__(FWD_NW * 64, 2) void fa_fwd_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    uint16_t* __restrict__ o, float* __restrict__ lse, int Hq, int Hkv, int Sq, int Sk_all,
-    int causal, float scale_log2, int n_bh, int n_qt, float* __restrict__ o_part,
-    float* __restrict__ lse_part, int n_split, int split_keys) {
+    const unsigned char* __restrict__ q, const unsigned char* __restrict__ k,
+    const unsigned char* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse, int Hq,
+    int Hkv, int Sq, int Sk_all, int causal, float scale_log2, float o_scale, int n_bh, int n_qt,
+    float* __restrict__ o_part, float* __restrict__ lse_part, int n_split, int split_keys) {
+  constexpr int DT = F::DT, HD = F::HD;
   constexpr int NW = FWD_NW;
   constexpr int QB = 1;
   constexpr int BR = FWD_BR;
   static_assert(NW == 8 && FWD_QB == 1, "two groups of four single-block waves");
-  // LDS: K stages at [0, 2 tiles), V stages at [2 tiles, 4 tiles)
-  using G = Geom<HD>;
+  // LDS: K stages at [0, 2 tiles), V stages at [2 tiles, 4 tiles); G is the
+  // layout of rows of ROW bytes (the 16-bit layout of the same row size)
+  using G = Geom<F::LAYOUT_HD>;
   constexpr int D = HD, ROW = G::ROW, TILE_BYTES = G::TILE;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * TILE_BYTES];
 
@@ -71,9 +140,9 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fa_fwd_kernel(
   // keys [kv0, kv0 + Sk) of the head, indexed from kv0 below
   const int kv0 = PART ? sp * split_keys : 0;
   const int Sk = PART ? max(0, min(Sk_all - kv0, split_keys)) : Sk_all;
-  const uint16_t* qh = q + (size_t)bh * Sq * D;
-  const uint16_t* kh = k + (((size_t)b * Hkv + hkv) * Sk_all + kv0) * D;
-  const uint16_t* vh = v + (((size_t)b * Hkv + hkv) * Sk_all + kv0) * D;
+  const unsigned char* qh = q + (size_t)bh * Sq * ROW;
+  const unsigned char* kh = k + (((size_t)b * Hkv + hkv) * Sk_all + kv0) * ROW;
+  const unsigned char* vh = v + (((size_t)b * Hkv + hkv) * Sk_all + kv0) * ROW;
   // key i (from kv0) is visible to row r iff i <= r + causal_off
   const int causal_off = Sk_all - Sq - kv0;
 
@@ -95,23 +164,20 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fa_fwd_kernel(
     n_wave = (wave_kv_end + KT - 1) / KT;
   }
 
-  // Q^T operands: lane holds Q[row][16*st + 8*g .. +7] for its query n; rows
-  // past Sq read as zeros
-  u32x4 qf[QB][G::DSTEPS];
+  // Q^T operands of the wave's query n; rows past Sq read as zeros
+  typename F::QFrag qf;
   {
     const __amdgpu_buffer_rsrc_t qr = make_rsrc(qh, (long long)Sq * ROW);
-    const unsigned row_off = (unsigned)((qw0 + n) * ROW + 16 * g);
-#pragma unroll
-    for (int st = 0; st < G::DSTEPS; ++st) qf[0][st] = load_b128(qr, row_off + 32 * st);
+    F::load_q(qf, qr, (unsigned)((qw0 + n) * ROW));
     vm_wait_all();  // Q is in registers before any tile load is issued
   }
 
-  f32x16 acc[G::DBLOCKS][QB];
+  f32x16 acc[F::DBLOCKS][QB];
   float m[QB], l[QB];
   m[0] = -INFINITY;
   l[0] = 0.0f;
 #pragma unroll
-  for (int db = 0; db < G::DBLOCKS; ++db) acc[db][0] = f32x16{};
+  for (int db = 0; db < F::DBLOCKS; ++db) acc[db][0] = f32x16{};
 
   // The loading waves split every tile: with L of them, chunk L*c + w covers
   // rows 4(L*c + w) + lane/16 (w = the wave's index among the loaders); L*c*4
@@ -121,14 +187,15 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fa_fwd_kernel(
   constexpr int CHUNKS_PER_LOADER = G::CHUNKS / LOADERS;
   static_assert(CHUNKS_PER_LOADER * LOADERS == G::CHUNKS && (LOADERS * G::RPC) % 16 == 0,
                 "whole chunks per loader, 16-row strides");
-  const unsigned koff = load_lane_offset<HD, false>(wave & (LOADERS - 1));
-  const unsigned voff = load_lane_offset<HD, true>(wave & (LOADERS - 1));
+  const unsigned koff = F::template load_offset<false>(wave & (LOADERS - 1));
+  const unsigned voff = F::template load_offset<true>(wave & (LOADERS - 1));
   unsigned char ATTN_LDS* lds = (unsigned char ATTN_LDS*)(smem);
-  auto issue = [&](const uint16_t* head, unsigned lane_off, int j, unsigned char ATTN_LDS* dst) {
+  auto issue = [&](const unsigned char* head, unsigned lane_off, int j,
+                   unsigned char ATTN_LDS* dst) {
     const int key0 = j * KT;
     // keys past Sk read as zeros
     const __amdgpu_buffer_rsrc_t r =
-        make_rsrc(head + (size_t)key0 * D, (long long)(Sk - key0) * ROW);
+        make_rsrc(head + (size_t)key0 * ROW, (long long)(Sk - key0) * ROW);
 #pragma unroll
     for (int c = 0; c < CHUNKS_PER_LOADER; ++c)
       load_chunk(r, lane_off + c * LOADERS * 1024,
@@ -136,11 +203,11 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fa_fwd_kernel(
   };
   auto k_stage = [&](int j) { return lds + (j & 1) * TILE_BYTES; };
   auto v_stage = [&](int j) { return lds + (2 + (j & 1)) * TILE_BYTES; };
-  const LaneAddr la = lane_addresses<HD>();
+  const LaneAddr la = F::lanes();
   const unsigned lds_base = (unsigned)(size_t)lds;
 
   f32x16 s[2][QB];
-  u32x4 pf[2][2][QB];
+  typename F::PFrag pf;
 
   // Every wave runs the same sequence  [MFMA(j)] barrier [softmax(j)] barrier,
   // group B one barrier later than group A, so each half-step pairs A's MFMA
@@ -232,7 +299,7 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fa_fwd_kernel(
   if (n_wave > 0) {
     mfma_begin(0);
     prio_hi();
-    qk_step<DT, QB, HD>(k_addr(0), la, qf, s);
+    F::qk(k_addr(0), la, qf, s);
     prio_lo();
     mfma_end();
     barrier();
@@ -243,8 +310,8 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fa_fwd_kernel(
     for (j = 1; j < n_wave; ++j) {
       mfma_begin(j);
       prio_hi();
-      pv_step<DT, QB, HD>(v_addr(j - 1), la, pf, acc);
-      qk_step<DT, QB, HD>(k_addr(j), la, qf, s);
+      F::pv(v_addr(j - 1), la, pf, acc);
+      F::qk(k_addr(j), la, qf, s);
       prio_lo();
       mfma_end();
       barrier();
@@ -254,7 +321,7 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fa_fwd_kernel(
       barrier();
       if (moved) {
 #pragma unroll
-        for (int db = 0; db < G::DBLOCKS; ++db) acc[db][0] *= alpha[0];
+        for (int db = 0; db < F::DBLOCKS; ++db) acc[db][0] *= alpha[0];
         ++j;
         break;
       }
@@ -262,8 +329,8 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fa_fwd_kernel(
     for (; j < n_wave; ++j) {
       mfma_begin(j);
       prio_hi();
-      pv_step<DT, QB, HD>(v_addr(j - 1), la, pf, acc);
-      qk_step<DT, QB, HD>(k_addr(j), la, qf, s);
+      F::pv(v_addr(j - 1), la, pf, acc);
+      F::qk(k_addr(j), la, qf, s);
       prio_lo();
       mfma_end();
       barrier();
@@ -274,7 +341,7 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fa_fwd_kernel(
     }
     mfma_begin(j);
     prio_hi();
-    pv_step<DT, QB, HD>(v_addr(j - 1), la, pf, acc);
+    F::pv(v_addr(j - 1), la, pf, acc);
     prio_lo();
     mfma_end();
     barrier();
@@ -296,13 +363,13 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fa_fwd_kernel(
   // epilogue: O = acc / l, rounded to the dtype; LSE = ln2 * (m + log2 l)
   if constexpr (PART) {
     const float lt = half_sum(l[0]);
-    const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+    const float inv = lt > 0.0f ? o_scale / lt : 0.0f;
     const int row = qw0 + n;
     if (row < Sq) {
       const size_t prow = ((size_t)bh * Sq + row) * n_split + sp;
       float* orow = o_part + prow * D;
 #pragma unroll
-      for (int db = 0; db < G::DBLOCKS; ++db)
+      for (int db = 0; db < F::DBLOCKS; ++db)
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
           const int d0 = 32 * db + 8 * jj + 4 * g;
@@ -317,12 +384,12 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fa_fwd_kernel(
     }
   } else {
     const float lt = half_sum(l[0]);
-    const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+    const float inv = lt > 0.0f ? o_scale / lt : 0.0f;
     const int row = qw0 + n;
     if (row < Sq) {
       uint16_t* orow = o + ((size_t)bh * Sq + row) * D;
 #pragma unroll
-      for (int db = 0; db < G::DBLOCKS; ++db)
+      for (int db = 0; db < F::DBLOCKS; ++db)
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
           const int d0 = 32 * db + 8 * jj + 4 * g;
@@ -338,29 +405,32 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fa_fwd_kernel(
   }
 }
 
-template <int DT, int HD, bool PART>
+template <typename F, bool PART>
 static void launch_fwd_t(const FwdArgs& a, const FwdSplitArgs* sa, hipStream_t stream) {
   const int n_bh = a.B * a.Hq;
   const int n_qt = (a.Sq + FWD_BR - 1) / FWD_BR;
   const int n_split = PART ? sa->num_splits : 1;
   const long long items = (long long)n_bh * n_qt * n_split;
   dim3 grid((unsigned)items), block(FWD_NW * 64);
-  hipLaunchKernelGGL((fa_fwd_kernel<DT, HD, PART>), grid, block, 0, stream,
-                     static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-                     static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.lse, a.Hq,
-                     a.Hkv, a.Sq, a.Sk, a.causal, a.scale_log2, n_bh, n_qt,
+  hipLaunchKernelGGL((fa_fwd_kernel<F, PART>), grid, block, 0, stream,
+                     static_cast<const unsigned char*>(a.q), static_cast<const unsigned char*>(a.k),
+                     static_cast<const unsigned char*>(a.v), static_cast<uint16_t*>(a.o), a.lse,
+                     a.Hq, a.Hkv, a.Sq, a.Sk, a.causal, a.scale_log2, a.o_scale, n_bh, n_qt,
                      PART ? sa->o_part : nullptr, PART ? sa->lse_part : nullptr, n_split,
                      PART ? sa->split_keys : 0);
 }
 
 template <bool PART>
 static hipError_t launch_fwd_any(const FwdArgs& a, const FwdSplitArgs* sa, hipStream_t stream) {
-  if (a.d == 64)
-    a.dtype == 0 ? launch_fwd_t<0, 64, PART>(a, sa, stream)
-                 : launch_fwd_t<1, 64, PART>(a, sa, stream);
+  if (a.fp8)
+    a.dtype == 0 ? launch_fwd_t<In8<0>, PART>(a, sa, stream)
+                 : launch_fwd_t<In8<1>, PART>(a, sa, stream);
+  else if (a.d == 64)
+    a.dtype == 0 ? launch_fwd_t<In16<0, 64>, PART>(a, sa, stream)
+                 : launch_fwd_t<In16<1, 64>, PART>(a, sa, stream);
   else
-    a.dtype == 0 ? launch_fwd_t<0, 128, PART>(a, sa, stream)
-                 : launch_fwd_t<1, 128, PART>(a, sa, stream);
+    a.dtype == 0 ? launch_fwd_t<In16<0, 128>, PART>(a, sa, stream)
+                 : launch_fwd_t<In16<1, 128>, PART>(a, sa, stream);
   return hipGetLastError();
 }
 

@@ -18,8 +18,10 @@ struct FwdArgs {
   float* lse;
   int B, Hq, Hkv, Sq, Sk, d;
   int causal;
-  float scale_log2;  // scale * log2(e), rounded once to fp32 on the host
-  int dtype;
+  float scale_log2;  // scale * log2(e) (* Q and K descales in FP8), rounded once to fp32 on the host
+  int dtype;         // of O (and of Q, K, V unless fp8)
+  float o_scale = 1.0f;  // multiplies O (V's descale in FP8)
+  int fp8 = 0;           // Q, K, V are OCP E4M3 (head dimension 128)
 };
 
 // split-KV prefill: partial outputs of num_splits key ranges of split_keys

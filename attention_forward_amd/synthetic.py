@@ -101,3 +101,44 @@ def bits(t: torch.Tensor):
     import numpy as np
 
     return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+# FP8: the headline prefill shape with OCP E4M3 inputs and bf16 output (the
+# FP8 variant of the method; the pages measure no FP8 workload of their own).
+FP8_WORKLOADS = {
+    "fwd_fp8_causal_b2_h16_s8192": Workload("fwd_fp8_causal_b2_h16_s8192", 2, 16, 16, 8192, 8192,
+                                            128, BF16, True, 8),
+}
+
+
+def _quantise_e4m3(x: torch.Tensor):
+    """Per-tensor E4M3 quantisation of real inputs x: descale = amax / 448 (the
+    format's largest finite value), bytes = x / descale rounded by torch's
+    float8_e4m3fn cast.  Returns (uint8 tensor, descale)."""
+    amax = float(x.abs().max())
+    descale = amax / 448.0 if amax > 0 else 1.0
+    q8 = (x / descale).to(torch.float8_e4m3fn)
+    return q8.view(torch.uint8), descale
+
+
+def make_qkv_fp8(B, Hq, Hkv, Sq, Sk, d, seed):
+    """E4M3 inputs: Q, K, V drawn as make_qkv draws them (iid N(0,1), fp32), each
+    quantised per tensor.  Returns (q8, k8, v8) as CPU uint8 tensors and the
+    descales (q_descale, k_descale, v_descale); the real inputs are q8 * q_descale etc."""
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(int(seed))
+    out, scales = [], []
+    for shape in ((B, Hq, Sq, d), (B, Hkv, Sk, d), (B, Hkv, Sk, d)):
+        x = torch.empty(shape, dtype=torch.float32)
+        flat = x.view(-1, shape[-2], shape[-1])
+        for i in range(flat.shape[0]):
+            flat[i].copy_(torch.randn((shape[-2], shape[-1]), generator=gen, dtype=torch.float32))
+        t8, ds = _quantise_e4m3(x)
+        out.append(t8)
+        scales.append(ds)
+    return tuple(out), tuple(scales)
+
+
+def bytes_u8(t: torch.Tensor):
+    """A 1-byte tensor viewed as a numpy uint8 array."""
+    return t.contiguous().view(torch.uint8).numpy()

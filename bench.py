@@ -33,14 +33,15 @@ import numpy as np
 import torch
 
 import attention_forward_amd as A
-from attention_forward_amd.synthetic import (ALL_WORKLOADS, BF16, WORKLOADS, bits,
-                                             make_workload_inputs)
+from attention_forward_amd.synthetic import (ALL_WORKLOADS, BF16, FP8_WORKLOADS, TORCH_DTYPE,
+                                             WORKLOADS, bits, make_qkv_fp8, make_workload_inputs)
 
 PREFILL = WORKLOADS["fwd_bf16_causal_b2_h16_s8192"]
 DECODE = WORKLOADS["decode_bf16_b64_hq32_hkv8_sk8192_split16"]
 METRIC = "attention fwd TFLOP/s and % of MFMA ceiling (S=8k d=128); decode HBM GB/s"
 PEAK_MFMA_TFLOPS = 2500.0   # MI355X dense fp16/bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+FP8_PEAK_TFLOPS = 5000.0    # MI355X dense fp8 MFMA, published
 
 
 def prefill_algorithmic_bytes(w) -> int:
@@ -179,6 +180,18 @@ def other_workloads(iters=5):
                 out[name]["split"] = {"num_splits": ns, "ms": round(ms, 4),
                                       "tflops": round(w.flops / (ms * 1e-3) / 1e12, 2)}
                 del ws
+        del q, k, v, o, lse
+    for name, w in FP8_WORKLOADS.items():
+        (q, k, v), ds = make_qkv_fp8(w.B, w.Hq, w.Hkv, w.Sq, w.Sk, w.d, w.seed)
+        q, k, v = q.cuda(), k.cuda(), v.cuda()
+        o = torch.empty((w.B, w.Hq, w.Sq, w.d), device="cuda", dtype=TORCH_DTYPE[w.dtype])
+        lse = torch.empty((w.B, w.Hq, w.Sq), device="cuda", dtype=torch.float32)
+        ms = _time_ms(lambda: A.attn_fwd_fp8(q, k, v, causal=w.causal, scale=w.scale,
+                                             q_descale=ds[0], k_descale=ds[1], v_descale=ds[2],
+                                             out=o, lse=lse), iters, warmup=2)
+        tf = w.flops / (ms * 1e-3) / 1e12
+        out[name] = {"ms": round(ms, 4), "tflops": round(tf, 2),
+                     "frac_fp8_mfma_peak": round(tf / FP8_PEAK_TFLOPS, 4)}
         del q, k, v, o, lse
     return out
 

@@ -52,7 +52,7 @@ typedef enum {
   ATTN_ERR_NO_DEVICE = 6,   /* no HIP device visible */
   ATTN_ERR_HIP = 7,         /* a HIP call failed; see attn_last_error() */
   ATTN_ERR_VALUE = 8        /* bad scalar: causal not 0/1, scale negative or not finite,
-                               num_splits out of range */
+                               descale not positive, num_splits out of range */
 } attn_status;
 
 /*
@@ -70,6 +70,28 @@ typedef enum {
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int B, int Hq, int Hkv, int Sq, int Sk, int d, int causal, float scale,
              int dtype, void* stream);
+
+/*
+ * FP8 prefill: attn_fwd on OCP E4M3 ("E4M3FN": 1 sign, 4 exponent bits with
+ * bias 7, 3 fraction bits, no infinities, max 448) inputs with per-tensor
+ * scales.  The real inputs are q8 * q_descale, k8 * k_descale and
+ * v8 * v_descale; q, k, v hold the E4M3 bytes in the layouts above (1 byte per
+ * element).  Both products run on the FP8 matrix unit with fp32
+ * accumulation: the scores directly from the bytes (scale * q_descale *
+ * k_descale * log2(e) folded into one fp32 multiply), and P.V with the
+ * softmax weights rounded to E4M3 (they are at most 2^8 under the rescale
+ * threshold, inside the format's range); V's descale multiplies O before it
+ * is rounded to out_dtype.  LSE is fp32 as in attn_fwd.  The pages measured an
+ * FP8 arm and rejected it on their hardware, for lack of an 8-bit operand load
+ * and for accuracy ("The FA5090 Optimization Journey", scope and sec. 4, the
+ * hardware-generational gaps); the MI355X matrix unit runs FP8 at twice the
+ * 16-bit rate, and this entry point is judged by its own accuracy gate.
+ *   d = 128 only; out_dtype 0 (fp16) or 1 (bf16); descales finite and > 0.
+ */
+int attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int Hq, int Hkv, int Sq, int Sk, int d, int causal, float scale,
+                 float q_descale, float k_descale, float v_descale, int out_dtype,
+                 void* stream);
 
 /*
  * Split-KV prefill for grids too small to fill the chip (few batch*head

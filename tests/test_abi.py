@@ -29,7 +29,7 @@ def L():
 def declared_functions():
     text = open(os.path.join(ROOT, "include", "attn.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(attn_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_bound_functions():
@@ -100,6 +100,32 @@ def dec(L, **kw):
 ])
 def test_decode_validation(L, kw, status):
     assert dec(L, **kw) == status
+
+
+def f8(L, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=None, B=1, Hq=2, Hkv=1, Sq=8, Sk=8, d=128, causal=0,
+             scale=0.1, qd=1.0, kd=1.0, vd=1.0, dtype=1)
+    a.update(kw)
+    return L.attn_fwd_fp8(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+                          a["Sq"], a["Sk"], a["d"], a["causal"], a["scale"], a["qd"], a["kd"],
+                          a["vd"], a["dtype"], None)
+
+
+@cpu_only
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), A.ATTN_ERR_NULL), (dict(B=0), A.ATTN_ERR_SHAPE),
+    (dict(Hq=3, Hkv=2), A.ATTN_ERR_SHAPE), (dict(d=64), A.ATTN_ERR_UNSUPPORTED),
+    (dict(dtype=2), A.ATTN_ERR_UNSUPPORTED), (dict(causal=3), A.ATTN_ERR_VALUE),
+    (dict(scale=-1.0), A.ATTN_ERR_VALUE), (dict(qd=0.0), A.ATTN_ERR_VALUE),
+    (dict(kd=-2.0), A.ATTN_ERR_VALUE), (dict(vd=float("inf")), A.ATTN_ERR_VALUE),
+    (dict(qd=1e30, kd=1e30), A.ATTN_ERR_VALUE),
+    (dict(v=ctypes.c_void_p((1 << 20) + 4)), A.ATTN_ERR_ALIGN),
+    (dict(Sk=1 << 24), A.ATTN_ERR_SHAPE), (dict(dtype=0), A.ATTN_ERR_NO_DEVICE),
+    (dict(causal=1), A.ATTN_ERR_NO_DEVICE), (dict(), A.ATTN_ERR_NO_DEVICE),
+])
+def test_fp8_validation(L, kw, status):
+    assert f8(L, **kw) == status
+    assert A.last_error() != ""
 
 
 def spl(L, **kw):
