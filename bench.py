@@ -81,7 +81,7 @@ def measured_traffic(path=None):
         hits = [v for name, v in k.items() if name.startswith(prefix)]
         return hits[0] if len(hits) == 1 else None
 
-    fwd = find("attn::fa_fwd_kernel<1")
+    fwd = find("attn::fa_fwd_kernel<attn::In16<1, 128>, false>")
     split = find("attn::fa_decode_split_kernel<1")
     comb = find("attn::fa_combine_kernel<1")
     pre = None if fwd is None else {"bytes": round(fwd["read_bytes"] + fwd["write_bytes"]),
@@ -145,7 +145,7 @@ def hbm_read_ceiling(gib=4, iters=10):
     return best
 
 
-def other_workloads(iters=5):
+def other_workloads(iters=20):
     """Throughput of the other workloads (context; their parity is checked by the
     GPU tests): the other prefill shapes in TFLOP/s, and the headline prefill
     and decode shapes at head dimension 64 (TFLOP/s, GB/s)."""
@@ -160,14 +160,14 @@ def other_workloads(iters=5):
             ws = torch.empty(A.attn_decode_workspace_bytes(w.B, w.Hq, w.d, w.num_splits),
                              device="cuda", dtype=torch.uint8)
             ms = _time_ms(lambda: A.attn_fwd_decode(q, k, v, w.num_splits, scale=w.scale, out=o,
-                                                    lse=lse, workspace=ws), iters, warmup=2)
+                                                    lse=lse, workspace=ws), iters, warmup=10)
             out[name] = {"ms": round(ms, 4),
                          "gbs": round(decode_algorithmic_bytes(w) / (ms * 1e-3) / 1e9, 1)}
             del ws
         else:
             lse = torch.empty(q.shape[:3], device="cuda", dtype=torch.float32)
             ms = _time_ms(lambda: A.attn_fwd(q, k, v, causal=w.causal, scale=w.scale, out=o,
-                                             lse=lse), iters, warmup=2)
+                                             lse=lse), iters, warmup=10)
             out[name] = {"ms": round(ms, 4), "tflops": round(w.flops / (ms * 1e-3) / 1e12, 2)}
             # under-filled grids: the split-KV form with the recommended split count
             ns = A.attn_fwd_num_splits(w.B, w.Hq, w.Sq, w.Sk, w.d)
@@ -176,7 +176,7 @@ def other_workloads(iters=5):
                                  device="cuda", dtype=torch.uint8)
                 ms = _time_ms(lambda: A.attn_fwd_split(q, k, v, ns, causal=w.causal,
                                                        scale=w.scale, out=o, lse=lse,
-                                                       workspace=ws), iters, warmup=2)
+                                                       workspace=ws), iters, warmup=10)
                 out[name]["split"] = {"num_splits": ns, "ms": round(ms, 4),
                                       "tflops": round(w.flops / (ms * 1e-3) / 1e12, 2)}
                 del ws
@@ -188,7 +188,7 @@ def other_workloads(iters=5):
         lse = torch.empty((w.B, w.Hq, w.Sq), device="cuda", dtype=torch.float32)
         ms = _time_ms(lambda: A.attn_fwd_fp8(q, k, v, causal=w.causal, scale=w.scale,
                                              q_descale=ds[0], k_descale=ds[1], v_descale=ds[2],
-                                             out=o, lse=lse), iters, warmup=2)
+                                             out=o, lse=lse), iters, warmup=10)
         tf = w.flops / (ms * 1e-3) / 1e12
         out[name] = {"ms": round(ms, 4), "tflops": round(tf, 2),
                      "frac_fp8_mfma_peak": round(tf / FP8_PEAK_TFLOPS, 4)}

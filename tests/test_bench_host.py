@@ -29,9 +29,14 @@ def test_algorithmic_bytes_and_flops():
 def _traffic_file(tmp_path, sha):
     t = {"kernel_sources_sha256": sha, "copy_mib": 1024, "fetch_scale": 2.0, "write_scale": 1.0,
          "kernels": {
-             "attn::fa_fwd_kernel<1>": {"read_bytes": 4.0e8, "write_bytes": 6.0e7,
-                                        "dispatches": 3},
-             "attn::fa_fwd_kernel<0>": {"read_bytes": 1.0, "write_bytes": 1.0, "dispatches": 1},
+             "attn::fa_fwd_kernel<attn::In16<1, 128>, false>": {
+                 "read_bytes": 4.0e8, "write_bytes": 6.0e7, "dispatches": 3},
+             "attn::fa_fwd_kernel<attn::In16<0, 128>, false>": {
+                 "read_bytes": 1.0, "write_bytes": 1.0, "dispatches": 1},
+             "attn::fa_fwd_kernel<attn::In16<1, 128>, true>": {
+                 "read_bytes": 2.0, "write_bytes": 2.0, "dispatches": 1},
+             "attn::fa_fwd_kernel<attn::In8<1>, false>": {
+                 "read_bytes": 3.0, "write_bytes": 3.0, "dispatches": 1},
              "attn::fa_decode_split_kernel<1>": {"read_bytes": 2.0e9, "write_bytes": 1.0e7,
                                                  "dispatches": 3},
              "attn::fa_combine_kernel<1>": {"read_bytes": 1.0e7, "write_bytes": 5.0e5,
