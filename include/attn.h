@@ -83,8 +83,8 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  * threshold, inside the format's range); V's descale multiplies O before it
  * is rounded to out_dtype.  LSE is fp32 as in attn_fwd.  The pages measured an
  * FP8 arm and rejected it on their hardware, for lack of an 8-bit operand load
- * and for accuracy ("The FA5090 Optimization Journey", scope and sec. 4, the
- * hardware-generational gaps); the MI355X matrix unit runs FP8 at twice the
+ * and for accuracy ("The FA5090 Optimization Journey", scope and sec. 3, the
+ * comparison with FA3 and FA4); the MI355X matrix unit runs FP8 at twice the
  * 16-bit rate, and this entry point is judged by its own accuracy gate.
  *   d = 128 only; out_dtype 0 (fp16) or 1 (bf16); descales finite and > 0.
  */
