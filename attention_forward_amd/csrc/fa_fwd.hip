@@ -40,6 +40,10 @@ template <int DT_, int HD_>
 struct In16 {
   static constexpr int DT = DT_, HD = HD_, LAYOUT_HD = HD_, DBLOCKS = HD_ / 32;
   static constexpr bool FP8 = false;
+  // tile-load scheme (ATTN_LOADERS values, measured per format): both groups
+  // in their softmax phases at d = 128 (+2.4%), group B alone at d = 64 (the
+  // other scheme loses 9% there)
+  static constexpr int LOAD_MODE = HD_ == 128 ? 3 : 1;
   using QFrag = u32x4[1][Geom<HD_>::DSTEPS];
   using PFrag = u32x4[2][2][1];
   __device__ static LaneAddr lanes() { return lane_addresses<HD_>(); }
@@ -68,6 +72,7 @@ template <int DT_>
 struct In8 {
   static constexpr int DT = DT_, HD = 128, LAYOUT_HD = 64, DBLOCKS = 4;
   static constexpr bool FP8 = true;
+  static constexpr int LOAD_MODE = 1;  // group B alone (both groups: -1.6%)
   using QFrag = u32x8[1][2];
   using PFrag = u32x8[1];
   __device__ static LaneAddr lanes() { return lane_addresses8(); }
@@ -120,7 +125,11 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fa_fwd_kernel(
   // layout of rows of ROW bytes (the 16-bit layout of the same row size)
   using G = Geom<F::LAYOUT_HD>;
   constexpr int D = HD, ROW = G::ROW, TILE_BYTES = G::TILE;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * TILE_BYTES];
+  // which waves issue the tile loads (see below), and ST stages per ring:
+  // three for the scheme that loads in both softmax phases, else two
+  constexpr int LM = ATTN_LOADERS >= 0 ? ATTN_LOADERS : F::LOAD_MODE;
+  constexpr int ST = LM == 3 ? 3 : 2;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * ST * TILE_BYTES];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -183,7 +192,7 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fa_fwd_kernel(
   // rows 4(L*c + w) + lane/16 (w = the wave's index among the loaders); L*c*4
   // is a multiple of 16 rows, so one swizzle pattern (and one lane offset)
   // serves all of a wave's chunks
-  constexpr int LOADERS = ATTN_LOADERS == 2 ? NW : NW / 2;
+  constexpr int LOADERS = LM >= 2 ? NW : NW / 2;
   constexpr int CHUNKS_PER_LOADER = G::CHUNKS / LOADERS;
   static_assert(CHUNKS_PER_LOADER * LOADERS == G::CHUNKS && (LOADERS * G::RPC) % 16 == 0,
                 "whole chunks per loader, 16-row strides");
@@ -201,8 +210,9 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fa_fwd_kernel(
       load_chunk(r, lane_off + c * LOADERS * 1024,
                  dst + (c * LOADERS + (wave & (LOADERS - 1))) * 1024);
   };
-  auto k_stage = [&](int j) { return lds + (j & 1) * TILE_BYTES; };
-  auto v_stage = [&](int j) { return lds + (2 + (j & 1)) * TILE_BYTES; };
+  auto stage = [](int j) { return ST == 2 ? (j & 1) : j % ST; };
+  auto k_stage = [&](int j) { return lds + stage(j) * TILE_BYTES; };
+  auto v_stage = [&](int j) { return lds + (ST + stage(j)) * TILE_BYTES; };
   const LaneAddr la = F::lanes();
   const unsigned lds_base = (unsigned)(size_t)lds;
 
@@ -226,27 +236,35 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fa_fwd_kernel(
   // wait.  ATTN_LOADERS: 0 = A loads everything, 1 = B does, 2 = both halves
   // (the issue of direct-to-LDS loads holds up the issuing wave for a while,
   // so the cost is best split between the two phases of the half-step).
-  constexpr bool A_LOADS = ATTN_LOADERS != 1, B_LOADS = ATTN_LOADERS != 0;
+  // ATTN_LOADERS 3 (with three stages per ring): both groups issue half of
+  // step j+1's loads, K(j+2) and V(j+1), at the start of their softmax phase
+  // j, and wait for them at the end of their next MFMA phase.  A's softmax
+  // phase j runs beside B's MFMA phase j, which reads K(j) and V(j-1); the
+  // stages written held K(j-1) and V(j-2), last read in MFMA phase j-1.  So
+  // each softmax phase carries half the issue cost, and the DMA writes into
+  // LDS land half beside each group's MFMA phase.
+  constexpr bool SOFTMAX_LOADS = LM == 3;
+  constexpr bool A_LOADS = LM != 1, B_LOADS = LM != 0;
   const bool loader = group_a ? A_LOADS : B_LOADS;
   auto issue_step = [&](int j) {
     if (j + 1 < n_tiles) issue(kh, koff, j + 1, k_stage(j + 1));
     if (j < n_tiles) issue(vh, voff, j, v_stage(j));
   };
   auto mfma_begin = [&](int j) {
-    if (A_LOADS && group_a) issue_step(j);
+    if (A_LOADS && !SOFTMAX_LOADS && group_a) issue_step(j);
   };
   auto mfma_end = [&]() {
-    if (B_LOADS && !group_a) vm_wait_all();
+    if (SOFTMAX_LOADS || (B_LOADS && !group_a)) vm_wait_all();
   };
   auto softmax_begin = [&](int j) {
-    if (B_LOADS && !group_a) issue_step(j + 1);
+    if (SOFTMAX_LOADS || (B_LOADS && !group_a)) issue_step(j + 1);
   };
   auto softmax_end = [&]() {
-    if (A_LOADS && group_a) vm_wait_all();
+    if (A_LOADS && !SOFTMAX_LOADS && group_a) vm_wait_all();
   };
   auto barrier = [] { __builtin_amdgcn_s_barrier(); };
-  auto k_addr = [&](int j) { return lds_base + (unsigned)((j & 1) * TILE_BYTES); };
-  auto v_addr = [&](int j) { return lds_base + (unsigned)((2 + (j & 1)) * TILE_BYTES); };
+  auto k_addr = [&](int j) { return lds_base + (unsigned)(stage(j) * TILE_BYTES); };
+  auto v_addr = [&](int j) { return lds_base + (unsigned)((ST + stage(j)) * TILE_BYTES); };
   float alpha[QB];
   auto masked = [&](int j) {
     const int key0 = j * KT;
@@ -281,6 +299,8 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fa_fwd_kernel(
 
   if (loader && n_tiles > 0) issue(kh, koff, 0, k_stage(0));
   vm_wait_all();
+  // A's half of step 0 (K(1), V(0)), waited at the end of its first MFMA phase
+  if (SOFTMAX_LOADS && group_a) issue_step(0);
   barrier();
   if (!group_a) {
     softmax_begin(-1);  // the half-step before B's first MFMA phase

@@ -62,9 +62,11 @@ hipError_t launch_decode_split(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 
 // Which wave groups of the prefill kernel issue the K/V tile loads
-// (0: group A, 1: group B, 2: both, half each).
+// (0: group A, 1: group B, 2: both, half each; 3: both, half each, in their
+// softmax phases, with three stages per ring).  -1: the scheme each input
+// format measured best with (its LOAD_MODE).
 #ifndef ATTN_LOADERS
-#define ATTN_LOADERS 1
+#define ATTN_LOADERS -1
 #endif
 
 // Number of 32-query blocks per wave and waves per workgroup of the prefill kernel.
@@ -77,10 +79,6 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 #ifndef ATTN_FWD_WPE
 #define ATTN_FWD_WPE 2
 #endif
-#ifndef ATTN_FWD_STAGES
-#define ATTN_FWD_STAGES 2
-#endif
-constexpr int FWD_STAGES = ATTN_FWD_STAGES;  // K/V tiles resident in LDS per workgroup
 constexpr int FWD_QB = ATTN_FWD_QB;
 constexpr int FWD_NW = ATTN_FWD_NW;
 constexpr int FWD_WAVES_PER_SIMD = ATTN_FWD_WPE;  // occupancy the register budget is sized for
