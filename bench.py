@@ -108,6 +108,16 @@ def _time_ms(fn, iters, warmup=3):
     return s.elapsed_time(e) / iters
 
 
+def _time_ms_median(fn, iters, warmup=3, rounds=5, rest_s=0.5):
+    """Median over `rounds` of _time_ms, after a short rest so that the clock
+    recovers from the workloads timed before (the context figures follow the
+    sustained headline steps and the GEMM ceilings)."""
+    torch.cuda.synchronize()
+    time.sleep(rest_s)
+    ts = sorted(_time_ms(fn, iters, warmup if r == 0 else 1) for r in range(rounds))
+    return ts[len(ts) // 2]
+
+
 def bmm_ceiling(dtype=torch.bfloat16, bh=32, n=8192, d=128, iters=10):
     """The attention-shaped product S = Q K^T of the headline workload as one
     batched GEMM ([32, 8192, 128] x [32, 128, 8192], both operands contiguous)."""
@@ -159,14 +169,14 @@ def other_workloads(iters=20):
             lse = torch.empty((w.B, w.Hq), device="cuda", dtype=torch.float32)
             ws = torch.empty(A.attn_decode_workspace_bytes(w.B, w.Hq, w.d, w.num_splits),
                              device="cuda", dtype=torch.uint8)
-            ms = _time_ms(lambda: A.attn_fwd_decode(q, k, v, w.num_splits, scale=w.scale, out=o,
+            ms = _time_ms_median(lambda: A.attn_fwd_decode(q, k, v, w.num_splits, scale=w.scale, out=o,
                                                     lse=lse, workspace=ws), iters, warmup=10)
             out[name] = {"ms": round(ms, 4),
                          "gbs": round(decode_algorithmic_bytes(w) / (ms * 1e-3) / 1e9, 1)}
             del ws
         else:
             lse = torch.empty(q.shape[:3], device="cuda", dtype=torch.float32)
-            ms = _time_ms(lambda: A.attn_fwd(q, k, v, causal=w.causal, scale=w.scale, out=o,
+            ms = _time_ms_median(lambda: A.attn_fwd(q, k, v, causal=w.causal, scale=w.scale, out=o,
                                              lse=lse), iters, warmup=10)
             out[name] = {"ms": round(ms, 4), "tflops": round(w.flops / (ms * 1e-3) / 1e12, 2)}
             # under-filled grids: the split-KV form with the recommended split count
@@ -174,7 +184,7 @@ def other_workloads(iters=20):
             if ns > 1:
                 ws = torch.empty(A.attn_fwd_split_workspace_bytes(w.B, w.Hq, w.Sq, w.d, ns),
                                  device="cuda", dtype=torch.uint8)
-                ms = _time_ms(lambda: A.attn_fwd_split(q, k, v, ns, causal=w.causal,
+                ms = _time_ms_median(lambda: A.attn_fwd_split(q, k, v, ns, causal=w.causal,
                                                        scale=w.scale, out=o, lse=lse,
                                                        workspace=ws), iters, warmup=10)
                 out[name]["split"] = {"num_splits": ns, "ms": round(ms, 4),
@@ -186,7 +196,7 @@ def other_workloads(iters=20):
         q, k, v = q.cuda(), k.cuda(), v.cuda()
         o = torch.empty((w.B, w.Hq, w.Sq, w.d), device="cuda", dtype=TORCH_DTYPE[w.dtype])
         lse = torch.empty((w.B, w.Hq, w.Sq), device="cuda", dtype=torch.float32)
-        ms = _time_ms(lambda: A.attn_fwd_fp8(q, k, v, causal=w.causal, scale=w.scale,
+        ms = _time_ms_median(lambda: A.attn_fwd_fp8(q, k, v, causal=w.causal, scale=w.scale,
                                              q_descale=ds[0], k_descale=ds[1], v_descale=ds[2],
                                              out=o, lse=lse), iters, warmup=10)
         tf = w.flops / (ms * 1e-3) / 1e12
