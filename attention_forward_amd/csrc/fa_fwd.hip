@@ -3,10 +3,11 @@
 // One workgroup of 8 waves per (batch*head, block of FWD_BR = 256 query rows);
 // wave w owns rows 32w..32w+31 and keeps their Q^T operands in registers for
 // the whole key loop.  64-key K and V tiles stream HBM -> LDS with
-// bounds-checked direct-to-LDS loads into two rings of two stages each, issued
-// two half-steps before their first use ("G5: Pipeline 重构与双缓冲", V21 and
-// V26: the next tile's load overlaps the current compute, and K and V have
-// separate readiness).
+// bounds-checked direct-to-LDS loads into a K ring and a V ring (two or three
+// stages each, by input format; see the load hooks below), issued two
+// half-steps before their first use ("G5: Pipeline 重构与双缓冲", V21 and V26:
+// the next tile's load overlaps the current compute, and K and V have separate
+// readiness).
 //
 // Ping-pong: waves w and w+4 share a SIMD.  Group A (waves 0-3) and group B
 // (waves 4-7) alternate between an MFMA phase, [O += P(j-1) V(j-1); S(j) = K(j)
