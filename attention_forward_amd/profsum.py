@@ -25,14 +25,25 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 
+def _code_only(text: str) -> str:
+    """C++ source without comments and with whitespace runs collapsed (string
+    literals in these sources hold no comment markers)."""
+    import re
+
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_sources_hash() -> str:
-    """sha256 over the HIP sources and headers the kernels are built from."""
+    """sha256 over the code (comments and layout ignored) of the HIP sources and
+    headers the kernels are built from."""
     h = hashlib.sha256()
     files = sorted(glob.glob(os.path.join(HERE, "csrc", "*.h")) +
                    glob.glob(os.path.join(HERE, "csrc", "*.hip")))
     for f in files:
         h.update(os.path.basename(f).encode())
-        h.update(open(f, "rb").read())
+        h.update(_code_only(open(f, encoding="utf-8").read()).encode())
     return h.hexdigest()
 
 
