@@ -244,6 +244,35 @@ def test_decode_small(shape):
     check_lse(lse.cpu().double().numpy().reshape(-1), lse_.reshape(-1), "decode")
 
 
+# Larger decode shapes: 16 splits of 128 keys with a ragged last tile, and 128
+# splits of 64 keys where the last holding keys has a partial tile and the one
+# after it is empty.
+DECODE_LARGER = [
+    # B, Hq, Hkv, Sk, num_splits, dtype, d
+    (32, 32, 8, 2038, 16, BF16, 128),
+    (4, 32, 8, 8100, 128, F16, 128),
+    (32, 32, 8, 2038, 16, F16, 64),
+]
+
+
+@pytest.mark.parametrize("shape", DECODE_LARGER,
+                         ids=lambda s: "B%d_Hq%d_Hkv%d_Sk%d_ns%d_d%d" % (s[:5] + s[6:]))
+def test_decode_many_items(shape):
+    B, Hq, Hkv, Sk, ns, dtype, d = shape
+    say("case decode many items", shape)
+    q, k, v = make_qkv(B, Hq, Hkv, 1, Sk, d, dtype, seed=250 + ns + d)
+    scale = 1.0 / math.sqrt(d)
+    o = torch.full((B, Hq, 1, d), float("nan"), device="cuda", dtype=TORCH_DTYPE[dtype])
+    lse = torch.full((B, Hq), float("nan"), device="cuda")
+    attn_fwd_decode(q.cuda(), k.cuda(), v.cuda(), ns, scale=scale, out=o, lse=lse)
+    torch.cuda.synchronize()
+    o_, lse_, o_ref = oracle.attention(bits(q), bits(k), bits(v), dtype, False, scale)
+    n = B * Hq
+    gate(o.cpu().double().numpy().reshape(n, d), o_.reshape(n, d), o_ref.reshape(n, d),
+         np.ones(n, bool), name="decode many items %s" % (shape,))
+    check_lse(lse.cpu().double().numpy().reshape(-1), lse_.reshape(-1), "decode many items")
+
+
 @pytest.mark.parametrize("d", [128, 64])
 @pytest.mark.parametrize("dtype", [F16, BF16])
 @pytest.mark.parametrize("S", [11, 16, 37, 70])
