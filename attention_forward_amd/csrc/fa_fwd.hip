@@ -73,7 +73,10 @@ template <int DT_>
 struct In8 {
   static constexpr int DT = DT_, HD = 128, LAYOUT_HD = 64, DBLOCKS = 4;
   static constexpr bool FP8 = true;
-  static constexpr int LOAD_MODE = 1;  // group B alone (both groups: -1.6%)
+  // group A at the start of its MFMA phase, which at twice the 16-bit rate
+  // leaves it waiting at the barrier anyway (+2.2% over group B in its softmax
+  // phase; both groups in their softmax phases: -1.6%)
+  static constexpr int LOAD_MODE = 0;
   using QFrag = u32x8[1][2];
   using PFrag = u32x8[1];
   __device__ static LaneAddr lanes() { return lane_addresses8(); }
