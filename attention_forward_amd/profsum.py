@@ -8,6 +8,9 @@
     python -m attention_forward_amd.profsum traffic DIR FETCH_NAME WRITE_NAME --copy-mib 1024 \
         --cmd-fetch "<command>" --cmd-write "<command>" --out profiles/traffic.json > profiles/Y.md
 
+    # per-kernel means of any counters, one --pmc run per NAME
+    python -m attention_forward_amd.profsum counters DIR NAME[@SUBSTR] ... --cmd "<c1>" --cmd "<c2>"
+
 Only parses files; it runs nothing on the GPU.
 """
 from __future__ import annotations
@@ -137,9 +140,60 @@ def traffic(d, fetch_name, write_name, copy_mib, cmd_fetch, cmd_write, out_json)
     return "\n".join(lines) + "\n"
 
 
+def counters(d, names, cmds, match=("attn::",), xcc=8, simds=1024):
+    """Per-kernel mean over dispatches of every counter in one or more --pmc runs
+    (one run per name, each within the hardware's per-block counter limits).
+
+    GRBM_GUI_ACTIVE is summed over the XCDs in the CSV, so its per-XCD value over
+    the dispatch's duration is the effective shader clock (slightly high for short
+    dispatches, whose counter window includes the launch); MFMA busy is
+    SQ_VALU_MFMA_BUSY_CYCLES (summed over SIMDs) over SIMDs x per-XCD cycles."""
+    out = ["# Hardware counters per dispatch", "", "Commands (one counter pass each):", "", "```"]
+    out += list(cmds) + ["```", ""]
+    for name in names:
+        name, _, only = name.partition("@")  # NAME@SUBSTR: this pass's kernels must hold SUBSTR
+        pass_match = (only,) if only else match
+        path = os.path.join(d, name + "_counter_collection.csv")
+        agg = _counters(path)
+        dur = collections.defaultdict(dict)
+        for r in csv.DictReader(open(path)):
+            dur[r["Kernel_Name"]][r["Dispatch_Id"]] = (int(r["End_Timestamp"]) -
+                                                       int(r["Start_Timestamp"]))
+        out += ["Pass `%s`:" % name, ""]
+        kernels = [k for k in agg if any(m in k for m in pass_match)]
+        cols = sorted({c for k in kernels for c in agg[k]})
+        derived = []
+        if "GRBM_GUI_ACTIVE" in cols:
+            derived.append("clock GHz")
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in cols:
+                derived.append("MFMA busy")
+        out.append("| kernel | dispatches | mean µs | " + " | ".join(cols + derived) + " |")
+        out.append("|---|---|---|" + "---|" * (len(cols) + len(derived)))
+        for k in kernels:
+            n = max(len(v) for v in agg[k].values())
+            mean = {c: sum(v) / len(v) for c, v in agg[k].items() if v}
+            ns = sum(dur[k].values()) / len(dur[k])
+            cells = ["%.4g" % mean[c] if c in mean else "" for c in cols]
+            if derived:
+                cyc = mean["GRBM_GUI_ACTIVE"] / xcc
+                cells.append("%.2f" % (cyc / ns))
+                if len(derived) > 1:
+                    cells.append("%.1f%%" % (100.0 * mean["SQ_VALU_MFMA_BUSY_CYCLES"] /
+                                             (simds * cyc)))
+            out.append("| `%s` | %d | %.1f | %s |" % (short(k)[:70], n, ns / 1e3, " | ".join(cells)))
+        out.append("")
+    return "\n".join(out)
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="what", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("dir")
+    c.add_argument("names", nargs="+")
+    c.add_argument("--cmd", action="append", required=True)
+    c.add_argument("--match", action="append", default=None,
+                   help="substring a kernel name must hold (repeatable; default attn::)")
     s = sub.add_parser("stats")
     s.add_argument("dir")
     s.add_argument("name")
@@ -157,6 +211,8 @@ def main():
     a = ap.parse_args()
     if a.what == "stats":
         sys.stdout.write(stats(a.dir, a.name, a.cmd, a.skip_first))
+    elif a.what == "counters":
+        sys.stdout.write(counters(a.dir, a.names, a.cmd, tuple(a.match or ["attn::"])))
     else:
         sys.stdout.write(traffic(a.dir, a.fetch_name, a.write_name, a.copy_mib, a.cmd_fetch,
                                  a.cmd_write, a.out))

@@ -214,10 +214,18 @@ def ratio(a, b):
 def gpu_state():
     """Clocks, power and temperature of GPU 0 as rocm-smi reports them (None
     where the tool is missing or fails); taken before and after the timed steps."""
+    import shutil
     import subprocess
 
+    # rocm-smi is a Python script behind an env shebang; starting it with this
+    # interpreter avoids the env process, which would replace itself by exec
+    # after a preloaded profiler library had already opened the GPU in it.
+    tool = shutil.which("rocm-smi")
+    if tool is None:
+        return None
     try:
-        r = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--showtemp", "--json"],
+        r = subprocess.run([sys.executable, os.path.realpath(tool), "--showclocks",
+                            "--showpower", "--showtemp", "--json"],
                            capture_output=True, text=True, timeout=30)
         data = json.loads(r.stdout)
     except Exception:  # no tool, no permission, or not JSON: report nothing

@@ -88,3 +88,30 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=300, cwd=ROOT)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_profsum_counters_means_clock_and_mfma_busy(tmp_path):
+    """The counter summary averages each counter over a kernel's dispatches and
+    derives the clock (GRBM cycles per XCD over the duration) and MFMA busy."""
+    from attention_forward_amd.profsum import counters
+
+    cols = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value", "Start_Timestamp",
+            "End_Timestamp"]
+    rows = []
+    for d, (grbm, busy) in enumerate([(8.0e6, 5.12e8), (8.8e6, 5.632e8)]):
+        # 500 us at 2.0 / 2.2 GHz on 8 XCDs; busy = half of 1024 SIMDs x cycles
+        for c, v in (("GRBM_GUI_ACTIVE", grbm), ("SQ_VALU_MFMA_BUSY_CYCLES", busy)):
+            rows.append([d, "void attn::k<1>(int)", c, v, 1000, 501000])
+            rows.append([d, "Cijk_gemm", c, 1.0, 0, 1000])
+    with open(tmp_path / "p_counter_collection.csv", "w") as fh:
+        fh.write(",".join(cols) + "\n")
+        for r in rows:
+            fh.write(",".join(str(x) for x in r) + "\n")
+    text = counters(str(tmp_path), ["p"], ["<cmd>"])
+    line = [x for x in text.splitlines() if "attn::k<1>" in x]
+    assert len(line) == 1 and "Cijk" not in text.split("Pass")[1]
+    cells = [c.strip() for c in line[0].strip("|").split("|")]
+    assert cells[1] == "2" and cells[2] == "500.0"  # dispatches, mean µs
+    assert cells[-2] == "2.10" and cells[-1] == "50.0%"
+    # NAME@SUBSTR selects other kernels for one pass
+    assert "Cijk_gemm" in counters(str(tmp_path), ["p@Cijk"], ["<cmd>"])
