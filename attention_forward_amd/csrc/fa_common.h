@@ -491,10 +491,22 @@ __device__ __forceinline__ bool softmax_step(f32x16 (&s)[2][QB], f32x16 (&o)[NDB
   const int lane = threadIdx.x & 63;
   const int g = lane >> 5;
   const int n = lane & 31;
+  // Score r of key block kb holds key key0 + 4g + off(kb, r), with the
+  // compile-time offset off = 32kb + 8(r >> 2) + (r & 3).  The key is hidden iff
+  // key >= n_keys or (causal) key > qi + causal_off, i.e. iff off > lim[qb]
+  // with lim = min(n_keys - 1, causal ? qi + causal_off : n_keys - 1) - key0 - 4g:
+  // one compare per score against a per-lane limit taken once per tile.
+  int lim[QB];
+  if constexpr (MASK) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int qi = qrow0 + 32 * qb + n;
+      const int last = causal ? min(n_keys - 1, qi + causal_off) : n_keys - 1;
+      lim[qb] = last - key0 - 4 * g;
+    }
+  }
   auto hidden = [&](int kb, int qb, int r) {
-    const int key = key0 + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
-    const int qi = qrow0 + 32 * qb + n;
-    return key >= n_keys || (causal && key > qi + causal_off);
+    return 32 * kb + 8 * (r >> 2) + (r & 3) > lim[qb];
   };
   if constexpr (MASK) {
 #pragma unroll
