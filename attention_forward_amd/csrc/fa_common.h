@@ -177,10 +177,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, lo
 }
 
 // 64 lanes x 16 bytes from rsrc at byte offsets voff -> LDS dst + 16 * lane
+// Cache policy of a load (the buffer instructions' cache-policy operand):
+// CP_NT marks a streaming, non-temporal read, for data read exactly once.
+constexpr int CP_DEFAULT = 0;
+constexpr int CP_NT = 2;
+
+template <int CP = CP_DEFAULT>
 __device__ __forceinline__ void load_chunk(__amdgpu_buffer_rsrc_t r, unsigned voff,
                                            unsigned char ATTN_LDS* dst) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, reinterpret_cast<ATTN_LDS void*>(dst), 16, (int)voff,
-                                           0, 0, 0);
+                                           0, 0, CP);
 }
 
 __device__ __forceinline__ u32x4 load_b128(__amdgpu_buffer_rsrc_t r, unsigned voff) {

@@ -87,18 +87,21 @@ __global__ __launch_bounds__(64, 2) void fa_decode_split_kernel(
   // complete in issue order (K(t), V(t), K(t+1), V(t+1), ...), so "K(t) has
   // landed" is vmcnt <= one tile half (V(t)) and "V(t) has landed" is
   // vmcnt <= one tile half (K(t+1)) or 0 on the last tile.
+  // Every K/V byte is read once per call, so the tile loads are marked
+  // non-temporal: measured on the 64 x 8 x 16-split workload, 6.1 against
+  // 5.7 TB/s with the default cache policy.
   constexpr int HALF = Gm::CHUNKS;  // load instructions per K or V tile
   auto issue_k = [&](int key0) {
     // keys past the split read as zeros
     const __amdgpu_buffer_rsrc_t r = make_rsrc(kh + (size_t)key0 * D, (long long)(j1 - key0) * ROW);
 #pragma unroll
     for (int c = 0; c < HALF; ++c)
-      load_chunk(r, koff[c % KP] + (c / KP) * 16 * ROW, kt + c * 1024);
+      load_chunk<CP_NT>(r, koff[c % KP] + (c / KP) * 16 * ROW, kt + c * 1024);
   };
   auto issue_v = [&](int key0) {
     const __amdgpu_buffer_rsrc_t r = make_rsrc(vh + (size_t)key0 * D, (long long)(j1 - key0) * ROW);
 #pragma unroll
-    for (int c = 0; c < HALF; ++c) load_chunk(r, voff + c * 1024, vt + c * 1024);
+    for (int c = 0; c < HALF; ++c) load_chunk<CP_NT>(r, voff + c * 1024, vt + c * 1024);
   };
   // every LDS read issued so far has returned (the stage may be overwritten)
   auto lds_drained = [] { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); };
