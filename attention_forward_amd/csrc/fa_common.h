@@ -457,7 +457,7 @@ __device__ __forceinline__ void store_p(u32x4 (&pf)[2][2][QB], int kb, int t, in
 }
 // FP8 MFMA: pf[qb] holds all 32 weights of the tile as E4M3 bytes, byte
 // 16kb + 8t + e for element 8t + e of key block kb (round to nearest even;
-// the weights are at most 2^8, inside the format's range).
+// the weights are at most 1 against the exact running max, inside the range).
 template <int DT, int QB>
 __device__ __forceinline__ void store_p(u32x8 (&pf)[QB], int kb, int t, int qb,
                                         const float (&w)[8]) {
@@ -482,11 +482,31 @@ __device__ __forceinline__ void store_p(u32x8 (&pf)[QB], int kb, int t, int qb,
 // a branch around it makes the register allocator move the whole accumulator
 // between two homes on every iteration, which costs more than it saves.
 //
+// With E4M3 weights (FP8 P fragments) the reference is the exact running max
+// (tau = 0): the E4M3 rounding of P is relative, so a weight of a row's top
+// key taken against a lagging reference lies between grid points and carries
+// up to 1/16 relative error, where against the exact max it is exactly 1.  On
+// a row dominated by a few keys that error reaches O almost undiminished
+// (measured on a CPU model of the kernel: about twice the mean row error of
+// rounding against the exact max).  In 16-bit the same offset costs at most
+// 2^-9 of a weight, so the lazy rule stays there.
+//
 // RESCALE_O = false leaves O alone and instead reports, as the return value,
 // whether any lane of the wave moved a finite reference max (the only case in
 // which O must be multiplied by alpha: a row whose max was -inf has O = 0).
 // The caller then applies alpha itself; until that happens alpha is exactly 1
 // for every lane, so skipping the multiply changes no bit.
+
+// threshold of the lazy reference max (log2 units) for a P fragment type
+template <typename PF>
+struct RescaleTau {
+  static constexpr float value = 8.0f;
+};
+template <int N>
+struct RescaleTau<u32x8[N]> {
+  static constexpr float value = 0.0f;  // E4M3 weights: the exact running max
+};
+
 template <int DT, int QB, bool MASK, bool RESCALE_O = true, int NDB = 4, typename PF>
 __device__ __forceinline__ bool softmax_step(f32x16 (&s)[2][QB], f32x16 (&o)[NDB][QB],
                                              float (&m)[QB], float (&l)[QB],
@@ -523,7 +543,7 @@ __device__ __forceinline__ bool softmax_step(f32x16 (&s)[2][QB], f32x16 (&o)[NDB
         for (int r = 0; r < 16; ++r)
           if (hidden(kb, qb, r)) s[kb][qb][r] = -INFINITY;
   }
-  constexpr float TAU = 8.0f;
+  constexpr float TAU = RescaleTau<PF>::value;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     float mx = fmaxf(s[0][qb][0], s[0][qb][1]);

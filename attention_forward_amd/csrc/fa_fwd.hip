@@ -281,7 +281,9 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fa_fwd_kernel(
     if (masked(j))
       return softmax_step<DT, QB, true, false>(s, acc, m, l, pf, scale_log2, key0, qw0, Sk,
                                                causal != 0, causal_off, alpha);
-    if (ATTN_FAST_SOFTMAX && !softmax_fast<DT, QB>(s, m, l, pf, scale_log2)) return false;
+    // the max-free form rests on the threshold rule, which FP8 does not use
+    if (ATTN_FAST_SOFTMAX && !F::FP8 && !softmax_fast<DT, QB>(s, m, l, pf, scale_log2))
+      return false;
     return softmax_step<DT, QB, false, false>(s, acc, m, l, pf, scale_log2, key0, qw0, Sk,
                                               false, 0, alpha);
   };
@@ -318,7 +320,9 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fa_fwd_kernel(
   // finite reference max moves, which for most rows never happens after their
   // first tile.  When it does, O is scaled once and the rest of the tiles run
   // in the second loop, which scales O on every tile as the recurrence is
-  // written.  The first tile needs no scaling: O is still zero.
+  // written.  The first tile needs no scaling: O is still zero.  (With the
+  // exact running max of FP8, a wave usually reaches the second loop within
+  // its first few tiles.)
   int j = 0;
   if (n_wave > 0) {
     mfma_begin(0);
