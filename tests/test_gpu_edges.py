@@ -155,3 +155,17 @@ def test_peaked_rows(dtype, causal, split):
     name = "peaked rows dtype %d causal %s split %d" % (dtype, causal, split)
     say("case", name)
     check_fwd(q, k, v, dtype, causal, 1.0 / math.sqrt(128), name, split)
+    if causal or split:
+        return
+    # the split-KV decode of each head's last query (6 key ranges, GQA 2)
+    B, Hq, _, d = q.shape
+    qd = q[:, :, -1:].contiguous()
+    o = torch.full((B, Hq, 1, d), float("nan"), device="cuda", dtype=t)
+    lse = torch.full((B, Hq), float("nan"), device="cuda")
+    attn_fwd_decode(qd.cuda(), k.cuda(), v.cuda(), 6, scale=1.0 / math.sqrt(128), out=o, lse=lse)
+    torch.cuda.synchronize()
+    o_, lse_, o_ref = oracle.attention(bits(qd), bits(k), bits(v), dtype, False, 1.0 / math.sqrt(128))
+    n = B * Hq
+    gate(o.cpu().double().numpy().reshape(n, d), o_.reshape(n, d), o_ref.reshape(n, d),
+         name=name + " decode")
+    check_lse(lse.cpu().double().numpy().reshape(-1), lse_.reshape(-1), name + " decode")
