@@ -152,3 +152,30 @@ DEFECTS = [
 def test_fp8_injected_defect_fails_the_gate_by_a_wide_margin(defect, growing, causal):
     r = gate_ratio(growing, 42, causal, BF16, defect)
     assert r > 5.0, (defect, r)
+
+
+def test_score_weight_closed_forms():
+    """The FP8 LSE tolerance's W on rows with closed forms: a row that sees one
+    key (W = |scale qd kd| sum_i |q_i k_i|), a row whose scores are all equal
+    (the plain mean over its keys), and a row that sees none (0)."""
+    from tests.test_gpu_fp8 import score_weight
+
+    e = lambda x: torch.tensor(x, dtype=torch.float32).to(torch.float8_e4m3fn).view(torch.uint8)
+    # Sq = 3 > Sk = 2, causal: row 0 sees nothing, row 1 key 0, row 2 keys 0 and 1
+    q = [[[[1.0, -2.0], [0.5, 4.0], [1.0, 0.0]]]]
+    k = [[[[3.0, 1.0], [-2.0, 8.0]]]]
+    q8, k8 = e(q), e(k)
+    scale, qd, kd = 0.5, 2.0, -0.25
+    c = abs(scale * qd * kd)
+    w = score_weight(q8, k8, (qd, kd, 1.0), True, scale, np.arange(3, dtype=np.int64))
+    assert w[0] == 0.0
+    assert w[1] == pytest.approx(c * (0.5 * 3.0 + 4.0 * 1.0))
+    # row 2: q = (1, 0) scores 3c' and -2c' differ; take the softmax by hand
+    s = np.array([3.0, -2.0]) * scale * qd * kd
+    p = np.exp(s - s.max()) / np.exp(s - s.max()).sum()
+    assert w[2] == pytest.approx(c * (p[0] * 3.0 + p[1] * 2.0))
+    # equal scores (q orthogonal to the difference of the keys): the plain mean
+    k8b = e([[[[2.0, 1.0], [2.0, -1.0]]]])
+    q8b = e([[[[1.0, 0.0]]]])
+    wb = score_weight(q8b, k8b, (1.0, 1.0, 1.0), False, 1.0, np.arange(1, dtype=np.int64))
+    assert wb[0] == pytest.approx((2.0 + 2.0) / 2)
