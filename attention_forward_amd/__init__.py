@@ -105,11 +105,60 @@ def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def _require(t, name):
-    if not t.is_cuda:
-        raise AttnError(ATTN_ERR_VALUE, "%s must be a device tensor" % name)
-    if not t.is_contiguous():
-        raise AttnError(ATTN_ERR_VALUE, "%s must be contiguous" % name)
+def _validate(*specs):
+    """Check tensor arguments before anything is launched.  Each spec is
+    (tensor or None, name, shape or None, dtypes or None).  First every shape
+    and dtype, then that all tensors sit on the first one's GPU and are
+    contiguous; so host tensors are also rejected with the precise reason.  The
+    C ABI only sees pointers, so this is the only guard against a wrongly sized
+    buffer."""
+    specs = [s for s in specs if s[0] is not None]
+    for t, name, shape, dtypes in specs:
+        if shape is not None and tuple(t.shape) != tuple(shape):
+            raise AttnError(ATTN_ERR_SHAPE, "%s has shape %s, expected %s"
+                            % (name, tuple(t.shape), tuple(shape)))
+        if dtypes is not None and t.dtype not in dtypes:
+            raise AttnError(ATTN_ERR_UNSUPPORTED, "%s has dtype %s, expected %s"
+                            % (name, t.dtype, " or ".join(str(x) for x in dtypes)))
+    dev = specs[0][0].device
+    for t, name, _, _ in specs:
+        if t.device != dev:
+            raise AttnError(ATTN_ERR_VALUE, "%s is on %s, expected %s" % (name, t.device, dev))
+        if not t.is_cuda:
+            raise AttnError(ATTN_ERR_VALUE, "%s must be a device tensor" % name)
+        if not t.is_contiguous():
+            raise AttnError(ATTN_ERR_VALUE, "%s must be contiguous" % name)
+
+
+def _rank(t, name, n):
+    if t.dim() != n:
+        raise AttnError(ATTN_ERR_SHAPE, "%s must have %d dimensions, has shape %s"
+                        % (name, n, tuple(t.shape)))
+
+
+def _qkv_shapes(q, k, v):
+    """q [B,Hq,Sq,d], k and v [B,Hkv,Sk,d] with one B and d; returns
+    (B, Hq, Sq, d, Hkv, Sk)."""
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _rank(t, nm, 4)
+    B, Hq, Sq, d = q.shape
+    Bk, Hkv, Sk, dk = k.shape
+    if Bk != B or dk != d or tuple(v.shape) != tuple(k.shape):
+        raise AttnError(ATTN_ERR_SHAPE, "q %s / k %s / v %s shapes disagree"
+                        % (tuple(q.shape), tuple(k.shape), tuple(v.shape)))
+    return B, Hq, Sq, d, Hkv, Sk
+
+
+def _workspace_size(ws, need):
+    if ws is not None and ws.numel() * ws.element_size() < need:
+        raise AttnError(ATTN_ERR_WORKSPACE, "workspace of %d bytes needed, %d given"
+                        % (need, ws.numel() * ws.element_size()))
+
+
+def _torch_dtypes():
+    import torch
+
+    return (torch.float16, torch.bfloat16)
 
 
 def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None,
@@ -118,19 +167,15 @@ def attn_fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None
 
     q [B,Hq,Sq,d], k and v [B,Hkv,Sk,d], contiguous fp16/bf16 device tensors.
     lse is fp32 [B,Hq,Sq] (None when want_lse is False).  Runs on the current
-    torch stream; returns without waiting for the kernel.
+    torch stream; returns without waiting for the kernel.  A caller-supplied
+    out must match q in shape, dtype and device, lse be fp32 [B,Hq,Sq].
     """
     import torch
 
-    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
-        _require(t, nm)
-    B, Hq, Sq, d = q.shape
-    Bk, Hkv, Sk, dk = k.shape
-    if Bk != B or dk != d or tuple(v.shape) != tuple(k.shape):
-        raise AttnError(ATTN_ERR_SHAPE, "q %s / k %s / v %s shapes disagree"
-                        % (tuple(q.shape), tuple(k.shape), tuple(v.shape)))
-    if k.dtype != q.dtype or v.dtype != q.dtype:
-        raise AttnError(ATTN_ERR_UNSUPPORTED, "q, k, v must share one dtype")
+    B, Hq, Sq, d, Hkv, Sk = _qkv_shapes(q, k, v)
+    _validate((q, "q", None, _torch_dtypes()), (k, "k", None, (q.dtype,)),
+              (v, "v", None, (q.dtype,)), (out, "out", q.shape, (q.dtype,)),
+              (lse, "lse", (B, Hq, Sq), (torch.float32,)))
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
@@ -151,21 +196,18 @@ def attn_fwd_fp8(q, k, v, causal: bool = False, scale: float | None = None,
     their per-tensor descales.  Returns (o in out_dtype (bf16 default), lse fp32)."""
     import torch
 
-    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
-        _require(t, nm)
-        if t.element_size() != 1:
-            raise AttnError(ATTN_ERR_UNSUPPORTED, "%s must hold 1-byte E4M3 values" % nm)
-    B, Hq, Sq, d = q.shape
-    Bk, Hkv, Sk, dk = k.shape
-    if Bk != B or dk != d or tuple(v.shape) != tuple(k.shape):
-        raise AttnError(ATTN_ERR_SHAPE, "q %s / k %s / v %s shapes disagree"
-                        % (tuple(q.shape), tuple(k.shape), tuple(v.shape)))
-    if scale is None:
-        scale = 1.0 / math.sqrt(d)
+    B, Hq, Sq, d, Hkv, Sk = _qkv_shapes(q, k, v)
     if out_dtype is None:
         out_dtype = out.dtype if out is not None else torch.bfloat16
-    code = ATTN_F16 if out_dtype == torch.float16 else ATTN_BF16 if out_dtype == torch.bfloat16 \
-        else -1
+    if out_dtype not in _torch_dtypes():
+        raise AttnError(ATTN_ERR_UNSUPPORTED, "output dtype %s (fp16 or bf16 only)" % out_dtype)
+    e4m3 = (torch.float8_e4m3fn, torch.uint8)
+    _validate((q, "q", None, e4m3), (k, "k", None, e4m3), (v, "v", None, e4m3),
+              (out, "out", (B, Hq, Sq, d), (out_dtype,)),
+              (lse, "lse", (B, Hq, Sq), (torch.float32,)))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    code = ATTN_F16 if out_dtype == torch.float16 else ATTN_BF16
     if out is None:
         out = torch.empty((B, Hq, Sq, d), dtype=out_dtype, device=q.device)
     if lse is None and want_lse:
@@ -190,26 +232,22 @@ def attn_fwd_split(q, k, v, num_splits: int | None = None, causal: bool = False,
                    want_lse: bool = True):
     """Split-KV prefill: attn_fwd's result from num_splits key ranges merged by LSE.
 
-    num_splits defaults to attn_fwd_num_splits(...).  `workspace` (uint8 device
+    num_splits defaults to attn_fwd_num_splits(...).  `workspace` (a device
     tensor of at least attn_fwd_split_workspace_bytes bytes) is allocated when
     omitted.  Returns (o, lse) like attn_fwd.
     """
     import torch
 
-    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
-        _require(t, nm)
-    B, Hq, Sq, d = q.shape
-    Bk, Hkv, Sk, dk = k.shape
-    if Bk != B or dk != d or tuple(v.shape) != tuple(k.shape):
-        raise AttnError(ATTN_ERR_SHAPE, "q %s / k %s / v %s shapes disagree"
-                        % (tuple(q.shape), tuple(k.shape), tuple(v.shape)))
-    if k.dtype != q.dtype or v.dtype != q.dtype:
-        raise AttnError(ATTN_ERR_UNSUPPORTED, "q, k, v must share one dtype")
+    B, Hq, Sq, d, Hkv, Sk = _qkv_shapes(q, k, v)
+    _validate((q, "q", None, _torch_dtypes()), (k, "k", None, (q.dtype,)),
+              (v, "v", None, (q.dtype,)), (out, "out", q.shape, (q.dtype,)),
+              (lse, "lse", (B, Hq, Sq), (torch.float32,)), (workspace, "workspace", None, None))
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if num_splits is None:
         num_splits = attn_fwd_num_splits(B, Hq, Sq, Sk, d)
     need = attn_fwd_split_workspace_bytes(B, Hq, Sq, d, num_splits)
+    _workspace_size(workspace, need)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     if out is None:
@@ -232,20 +270,21 @@ def attn_fwd_decode(q, k, v, num_splits: int, scale: float | None = None, out=No
                     workspace=None, want_lse: bool = True):
     """Single-token decode with split-KV; q [B,Hq,1,d], k/v [B,Hkv,Sk,d].
 
-    Returns (o [B,Hq,1,d], lse [B,Hq] fp32).  `workspace` (uint8 device tensor
-    of at least attn_decode_workspace_bytes bytes) is allocated when omitted.
+    Returns (o [B,Hq,1,d], lse [B,Hq] fp32).  `workspace` (a device tensor of
+    at least attn_decode_workspace_bytes bytes) is allocated when omitted.
     """
     import torch
 
-    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
-        _require(t, nm)
-    B, Hq, Sq, d = q.shape
+    B, Hq, Sq, d, Hkv, Sk = _qkv_shapes(q, k, v)
     if Sq != 1:
         raise AttnError(ATTN_ERR_SHAPE, "decode takes one query row (Sq = 1), got %d" % Sq)
-    _, Hkv, Sk, _ = k.shape
+    _validate((q, "q", None, _torch_dtypes()), (k, "k", None, (q.dtype,)),
+              (v, "v", None, (q.dtype,)), (out, "out", q.shape, (q.dtype,)),
+              (lse, "lse", (B, Hq), (torch.float32,)), (workspace, "workspace", None, None))
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     need = attn_decode_workspace_bytes(B, Hq, d, num_splits)
+    _workspace_size(workspace, need)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     if out is None:
@@ -263,14 +302,18 @@ def attn_splitkv_combine(o_part, lse_part, dtype, out=None, lse=None, want_lse: 
     """Merge fp32 partials o_part [B,Hq,S,d] / lse_part [B,Hq,S] -> (o [B,Hq,d], lse [B,Hq])."""
     import torch
 
-    _require(o_part, "o_part")
-    _require(lse_part, "lse_part")
+    _rank(o_part, "o_part", 4)
     B, Hq, S, d = o_part.shape
+    if dtype not in _torch_dtypes():
+        raise AttnError(ATTN_ERR_UNSUPPORTED, "output dtype %s (fp16 or bf16 only)" % dtype)
+    _validate((o_part, "o_part", None, (torch.float32,)),
+              (lse_part, "lse_part", (B, Hq, S), (torch.float32,)),
+              (out, "out", (B, Hq, d), (dtype,)), (lse, "lse", (B, Hq), (torch.float32,)))
     if out is None:
         out = torch.empty((B, Hq, d), dtype=dtype, device=o_part.device)
     if lse is None and want_lse:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=o_part.device)
-    code = ATTN_F16 if dtype == torch.float16 else ATTN_BF16 if dtype == torch.bfloat16 else -1
+    code = ATTN_F16 if dtype == torch.float16 else ATTN_BF16
     st = lib().attn_splitkv_combine(_ptr(o_part), _ptr(lse_part), _ptr(out), _ptr(lse), B, Hq, d,
                                     S, code, _stream(o_part.device))
     _check(st)

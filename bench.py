@@ -18,7 +18,7 @@ beside it.  The oracle's
 sample also checks the GPU output on those rows; a failing check prints no
 throughput.
 
-    python bench.py [--gpus 1] [--steps 100] [--warmup 30]
+    python bench.py [--gpus 1] [--steps 100] [--warmup 30] [--warmup-seconds 2]
 """
 from __future__ import annotations
 
@@ -248,12 +248,57 @@ def spread(xs):
     return {"median": round(pct(0.5), 4), "p10": round(pct(0.1), 4), "p90": round(pct(0.9), 4)}
 
 
-def gemm_ceiling(dtype, n=8192, iters=20):
+def warm_up(step, min_steps, min_seconds, settle=True, batch=20, tol=0.01, max_seconds=10.0):
+    """Untimed steps: at least `min_steps` and `min_seconds` of wall time; then,
+    with `settle`, batches of `batch` steps until two consecutive batches agree
+    within `tol` (or `max_seconds` have passed).  Returns what was run."""
+    t0 = time.perf_counter()
+    n = 0
+    while n < min_steps or time.perf_counter() - t0 < min_seconds:
+        step()
+        n += 1
+        if n % batch == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    batches = []
+    while settle and time.perf_counter() - t0 < max_seconds:
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(batch):
+            step()
+        e.record()
+        e.synchronize()
+        n += batch
+        batches.append(s.elapsed_time(e) / batch)
+        if len(batches) >= 2 and abs(batches[-1] - batches[-2]) <= tol * batches[-2]:
+            break
+    return {"steps": n, "seconds": round(time.perf_counter() - t0, 2),
+            "last_batches_ms": [round(x, 4) for x in batches[-2:]]}
+
+
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def gemm_ceiling(dtype, n=8192, iters=50, warm_s=0.5):
+    """hipBLASLt (torch.matmul) on an n^3 product, timed after at least warm_s
+    seconds of the same product so that the clock is in its loaded state, as it
+    is for the attention steps."""
     a = torch.randn(n, n, device="cuda", dtype=dtype)
     b = torch.randn(n, n, device="cuda", dtype=dtype)
-    for _ in range(3):
-        torch.matmul(a, b)
-    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < warm_s:
+        for _ in range(5):
+            torch.matmul(a, b)
+        torch.cuda.synchronize()
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     s.record()
     for _ in range(iters):
@@ -292,7 +337,7 @@ def cpu_baseline(q, k, v, o_gpu, target_s: float):
     bound = float(2 * np.abs(o_ref - o).max() + 1e-5)
     base = {
         "value": round(flops_per_row * n / dt / 1e12, 6), "unit": "TFLOP/s", "cores": nthreads,
-        "kind": "oracle",
+        "cpu": cpu_model(), "kind": "oracle",
         "sample": "%d uniform random query rows of %s (FP64, %.1f s wall, %d threads)"
                   % (n, w.name, dt, nthreads),
     }
@@ -318,7 +363,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=30,
-                    help="untimed steps first: the clock settles over the first dozen or so")
+                    help="untimed steps first (at least; see --warmup-seconds)")
+    ap.add_argument("--warmup-seconds", type=float, default=2.0,
+                    help="warm up for at least this long, and then until two consecutive "
+                         "batches of steps agree: the clock under sustained matrix load "
+                         "takes a second or more to settle, whatever the step count")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target wall time of the oracle's CPU-baseline sample")
     ap.add_argument("--skip-cpu-baseline", action="store_true",
@@ -364,10 +413,11 @@ def main():
         if ev:
             ev[2].record()
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warm = warm_up(step, args.warmup, args.warmup_seconds)
     state_before = None if args.skip_context else gpu_state()
+    # the state query leaves the GPU idle for a moment: bring the clock back
+    # under load before the timed steps
+    warm_up(step, 0, 0.3, settle=False)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -442,6 +492,7 @@ def main():
                                     "unit": "GB/s",
                                     "shape": stream_shape, "bytes": 4 << 30},
         "other_workloads": others,
+        "warmup_run": warm,
         "gpu_state": {"before": state_before, "after": state_after},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_MFMA_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_MFMA_TFLOPS, 4),
