@@ -1,7 +1,7 @@
 """Summarise rocprofv3 CSV output into the short text summaries kept under profiles/.
 
     # kernel durations (rocprofv3 --kernel-trace --stats -f csv ... -o NAME)
-    python -m attention_forward_amd.profsum stats DIR NAME --cmd "<command>" [--skip-first N] > profiles/X.md
+    python -m attention_forward_amd.profsum stats DIR NAME --cmd "<command>" [--skip-first N | --last N] > profiles/X.md
 
     # HBM bytes per dispatch from two --pmc runs (FETCH_SIZE, WRITE_SIZE), each scaled by
     # what the same counter reads for a plain copy of --copy-mib MiB run in the same process
@@ -56,7 +56,7 @@ def short(name: str) -> str:
     return name if i < 0 else name[:i]
 
 
-def stats(d, name, cmd, skip_first=0):
+def stats(d, name, cmd, skip_first=0, last=0):
     """The --stats table, and (with skip_first) the same averages over each kernel's
     dispatches after its first skip_first, from the kernel trace: the untimed
     warmup steps of a benchmark run drop out, so the figures compare with the
@@ -71,17 +71,21 @@ def stats(d, name, cmd, skip_first=0):
         out.append("| `%s` | %s | %.1f | %.1f | %.1f | %.1f%% |" % (
             short(r["Name"]), r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
             float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
-    if skip_first > 0:
+    if skip_first > 0 or last > 0:
         trace = os.path.join(d, name + "_kernel_trace.csv")
         per = collections.defaultdict(list)
         for r in csv.DictReader(open(trace)):
             per[short(r["Kernel_Name"])].append(
                 (int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
-        out += ["", "Dispatches after each kernel's first %d (the untimed warmup steps):" %
-                skip_first, "", "| kernel | calls | average µs | median µs | min µs | max µs |",
+        what = ("each kernel's last %d dispatches (the measured launches, after the warmup)" % last
+                if last > 0 else
+                "dispatches after each kernel's first %d (the untimed warmup steps)" % skip_first)
+        out += ["", what[0].upper() + what[1:] + ":", "",
+                "| kernel | calls | average µs | median µs | min µs | max µs |",
                 "|---|---|---|---|---|---|"]
         for k, v in per.items():
-            dur = sorted(x[1] for x in sorted(v)[skip_first:])
+            v = sorted(v)
+            dur = sorted(x[1] for x in (v[-last:] if last > 0 else v[skip_first:]))
             if not dur:
                 continue
             out.append("| `%s` | %d | %.1f | %.1f | %.1f | %.1f |" % (
@@ -200,6 +204,8 @@ def main():
     s.add_argument("--cmd", required=True)
     s.add_argument("--skip-first", type=int, default=0,
                    help="also average each kernel's dispatches after its first N")
+    s.add_argument("--last", type=int, default=0,
+                   help="also average each kernel's last N dispatches")
     t = sub.add_parser("traffic")
     t.add_argument("dir")
     t.add_argument("fetch_name")
@@ -210,7 +216,7 @@ def main():
     t.add_argument("--out", default=None)
     a = ap.parse_args()
     if a.what == "stats":
-        sys.stdout.write(stats(a.dir, a.name, a.cmd, a.skip_first))
+        sys.stdout.write(stats(a.dir, a.name, a.cmd, a.skip_first, a.last))
     elif a.what == "counters":
         sys.stdout.write(counters(a.dir, a.names, a.cmd, tuple(a.match or ["attn::"])))
     else:
