@@ -79,9 +79,9 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  * element).  Both products run on the FP8 matrix unit with fp32
  * accumulation: the scores directly from the bytes (scale * q_descale *
  * k_descale * log2(e) folded into one fp32 multiply), and P.V with the
- * softmax weights rounded to E4M3 (they are at most 2^8 under the rescale
- * threshold, inside the format's range); V's descale multiplies O before it
- * is rounded to out_dtype.  LSE is fp32 as in attn_fwd.  The pages measured an
+ * unnormalised softmax weights rounded to E4M3 (taken against the exact
+ * running max, so they are at most 1, inside the format's range); V's descale
+ * multiplies O before it is rounded to out_dtype.  LSE is fp32 as in attn_fwd.  The pages measured an
  * FP8 arm and rejected it on their hardware, for lack of an 8-bit operand load
  * and for accuracy ("The FA5090 Optimization Journey", scope and sec. 3, the
  * comparison with FA3 and FA4); the MI355X matrix unit runs FP8 at twice the

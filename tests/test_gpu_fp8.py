@@ -11,9 +11,9 @@ ref_fp8 rounds the unnormalised softmax weights to E4M3 before P.V and O to
 the output dtype.  LSE: |lse_gpu - lse| <= 1e-4 + 1e-6 |lse| + 2^-11 W, the
 16-bit tests' bound plus the error of the scores themselves.  The FP8 matrix
 unit's dot products are not correctly rounded fp32 sums: measured on random
-E4M3 vectors, a 64-term product is off by up to 2^-11.6 of its largest single
-term, and two chained ones (the 128 terms of a score) by up to 2^-12.6 of
-sum_i |q_i k_i|.  The LSE moves by at most the softmax-weighted mean of its
+E4M3 vectors (tests/test_gpu_mfma_precision.py, which keeps checking it), a
+64-term product is off by up to 2^-11.6 of its largest single term, and two
+chained ones (the 128 terms of a score) by up to 2^-12.6 of sum_i |q_i k_i|.  The LSE moves by at most the softmax-weighted mean of its
 scores' errors, so W is sum_j softmax_j * |scale q_descale k_descale| *
 sum_i |q_i k_ji| over the row's visible keys, and 2^-11 leaves a factor of 3
 over that worst case.  (The kernel's LSE on the peaked rows below stays within
