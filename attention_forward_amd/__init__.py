@@ -32,8 +32,8 @@ ATTN_F16 = 0
 ATTN_BF16 = 1
 
 EXPORTED = ("attn_fwd", "attn_fwd_fp8", "attn_fwd_split", "attn_fwd_split_workspace_bytes", "attn_fwd_num_splits",
-            "attn_decode_workspace_bytes", "attn_fwd_decode", "attn_splitkv_combine",
-            "attn_last_error")
+            "attn_decode_workspace_bytes", "attn_fwd_decode", "attn_fwd_decode_noalloc",
+            "attn_decode_scratch_bytes", "attn_splitkv_combine", "attn_last_error")
 
 _lib = None
 
@@ -68,6 +68,10 @@ def lib() -> ctypes.CDLL:
     L.attn_decode_workspace_bytes.restype = sz
     L.attn_fwd_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, sz, vp]
     L.attn_fwd_decode.restype = i
+    L.attn_fwd_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp]
+    L.attn_fwd_decode_noalloc.restype = i
+    L.attn_decode_scratch_bytes.argtypes = []
+    L.attn_decode_scratch_bytes.restype = sz
     L.attn_splitkv_combine.argtypes = [vp, vp, vp, vp, i, i, i, i, i, vp]
     L.attn_splitkv_combine.restype = i
     L.attn_last_error.argtypes = []
@@ -294,6 +298,35 @@ def attn_fwd_decode(q, k, v, num_splits: int, scale: float | None = None, out=No
     st = lib().attn_fwd_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Sk, d,
                                float(scale), _dtype_code(q), int(num_splits), _ptr(workspace),
                                workspace.numel() * workspace.element_size(), _stream(q.device))
+    _check(st)
+    return out, lse
+
+
+def attn_decode_scratch_bytes() -> int:
+    return int(lib().attn_decode_scratch_bytes())
+
+
+def attn_fwd_decode_noalloc(q, k, v, num_splits: int, out, lse=None, scale: float | None = None):
+    """attn_fwd_decode with the split partials in the library's own per-GPU
+    scratch: no workspace and no allocation, for callers that cannot allocate
+    (graph capture, allocation-free loops).  `out` ([B,Hq,1,d], q's dtype) is
+    required and `lse` (fp32 [B,Hq]) optional, both supplied by the caller.
+    Calls that overlap on one GPU share the scratch and race."""
+    import torch
+
+    B, Hq, Sq, d, Hkv, Sk = _qkv_shapes(q, k, v)
+    if Sq != 1:
+        raise AttnError(ATTN_ERR_SHAPE, "decode takes one query row (Sq = 1), got %d" % Sq)
+    if out is None:
+        raise AttnError(ATTN_ERR_NULL, "attn_fwd_decode_noalloc needs the output buffer")
+    _validate((q, "q", None, _torch_dtypes()), (k, "k", None, (q.dtype,)),
+              (v, "v", None, (q.dtype,)), (out, "out", q.shape, (q.dtype,)),
+              (lse, "lse", (B, Hq), (torch.float32,)))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = lib().attn_fwd_decode_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq,
+                                       Hkv, Sk, d, float(scale), _dtype_code(q), int(num_splits),
+                                       _stream(q.device))
     _check(st)
     return out, lse
 

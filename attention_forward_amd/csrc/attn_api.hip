@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <mutex>
 
 #include "attn.h"
 #include "launch.h"
@@ -47,6 +48,113 @@ constexpr size_t kAlign = 256;
 // is 32-bit: S * 256 bytes must stay below 2^32
 constexpr int kMaxSeq = (1 << 24) - 1;
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// ---- the library-owned decode scratch (attn_fwd_decode_noalloc) ----
+// One fixed buffer per GPU for the split partials of callers that cannot
+// allocate.  In host code `scratch` names a host-side stand-in, not device
+// memory: its device address is looked up once per device with
+// hipGetSymbolAddress (with that device current) and only that address is
+// handed to kernels.  Every call on a GPU shares the buffer; the split kernel
+// writes every partial it covers, so nothing needs clearing between calls.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_addr[kMaxDevices] = {};
+
+// device address of this library's scratch on the device `stream` runs on
+int scratch_address(hipStream_t stream, const char* fn, void** out) {
+  int dev = 0;
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(ATTN_ERR_HIP, "%s: device of the stream: %s", fn,
+                                   hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(ATTN_ERR_UNSUPPORTED, "%s: device %d (at most %d devices)", fn, dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_addr[dev] == nullptr) {
+    int cur = 0;
+    e = hipGetDevice(&cur);
+    if (e == hipSuccess && cur != dev) e = hipSetDevice(dev);
+    void* p = nullptr;
+    if (e == hipSuccess) e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    const hipError_t restore = cur != dev ? hipSetDevice(cur) : hipSuccess;
+    if (e != hipSuccess || p == nullptr)
+      return fail(ATTN_ERR_HIP, "%s: address of the decode scratch on device %d: %s", fn, dev,
+                  hipGetErrorString(e));
+    if (restore != hipSuccess)
+      return fail(ATTN_ERR_HIP, "%s: restoring device %d: %s", fn, cur,
+                  hipGetErrorString(restore));
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return ATTN_OK;
+}
+
+size_t decode_workspace_bytes(int B, int Hq, int d, int num_splits) {
+  if (B <= 0 || Hq <= 0 || d <= 0 || num_splits <= 0) return 0;
+  const size_t rows = (size_t)B * Hq * num_splits;
+  return round_up(rows * d * sizeof(float)) + round_up(rows * sizeof(float));
+}
+
+// attn_fwd_decode with the caller's workspace, or (noalloc) the library's scratch
+int decode(const char* fn, const void* q, const void* k, const void* v, void* o, float* lse, int B,
+           int Hq, int Hkv, int Sk, int d, float scale, int dtype, int num_splits,
+           void* workspace, size_t workspace_bytes, void* stream, bool noalloc) {
+  g_err[0] = '\0';
+  if (!q || !k || !v || !o) return fail(ATTN_ERR_NULL, "%s: q, k, v and o must be non-NULL", fn);
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Sk <= 0 || d <= 0)
+    return fail(ATTN_ERR_SHAPE, "%s: sizes must be positive", fn);
+  if (Hq % Hkv != 0)
+    return fail(ATTN_ERR_SHAPE, "%s: Hq=%d is not a multiple of Hkv=%d", fn, Hq, Hkv);
+  if (dtype != ATTN_F16 && dtype != ATTN_BF16)
+    return fail(ATTN_ERR_UNSUPPORTED, "%s: dtype %d", fn, dtype);
+  if (!attn::head_dim_supported(d))
+    return fail(ATTN_ERR_UNSUPPORTED, "%s: head dim %d (64 and 128 are implemented)", fn, d);
+  if (Hq / Hkv > 32)
+    return fail(ATTN_ERR_UNSUPPORTED, "%s: query heads per kv head %d > 32", fn, Hq / Hkv);
+  if (num_splits < 1 || num_splits > Sk)
+    return fail(ATTN_ERR_VALUE, "%s: num_splits=%d not in [1, Sk=%d]", fn, num_splits, Sk);
+  if (!std::isfinite(scale) || scale < 0.0f)
+    return fail(ATTN_ERR_VALUE, "%s: scale must be finite and >= 0", fn);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+      (lse && !aligned4(lse)))
+    return fail(ATTN_ERR_ALIGN, "%s: q, k, v, o must be 16-byte aligned, lse 4-byte", fn);
+  const size_t need = decode_workspace_bytes(B, Hq, d, num_splits);
+  if (noalloc) {
+    if (need > kScratchBytes)
+      return fail(ATTN_ERR_WORKSPACE,
+                  "%s: the split partials need %zu bytes, above the library's %zu-byte scratch "
+                  "(fewer splits or a smaller batch fit; attn_fwd_decode takes a workspace)",
+                  fn, need, kScratchBytes);
+  } else {
+    if (!workspace || workspace_bytes < need)
+      return fail(ATTN_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (!aligned16(workspace)) return fail(ATTN_ERR_ALIGN, "%s: misaligned workspace", fn);
+  }
+  if ((long long)B * Hkv * num_splits > INT_MAX || (long long)B * Hq > INT_MAX ||
+      (long long)B * Hkv * Sk * d > (1LL << 46))
+    return fail(ATTN_ERR_SHAPE, "%s: problem too large for one launch", fn);
+  if (Sk > kMaxSeq) return fail(ATTN_ERR_SHAPE, "%s: Sk above %d", fn, kMaxSeq);
+  int st = check_device();
+  if (st != ATTN_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (noalloc) {
+    st = scratch_address(s, fn, &workspace);
+    if (st != ATTN_OK) return st;
+  }
+  const size_t rows = (size_t)B * Hq * num_splits;
+  float* o_part = static_cast<float*>(workspace);
+  float* lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                             round_up(rows * d * sizeof(float)));
+  attn::DecodeArgs da{q, k, v, o_part, lse_part, B, Hq, Hkv, Sk, d, num_splits,
+                      fold_log2e(scale), dtype};
+  st = hip_status(attn::launch_decode_split(da, s), "decode split launch");
+  if (st != ATTN_OK) return st;
+  attn::CombineArgs ca{o_part, lse_part, o, lse, B * Hq, num_splits, d, dtype};
+  return hip_status(attn::launch_combine(ca, s), "decode combine launch");
+}
 
 }  // namespace
 
@@ -207,9 +315,7 @@ int attn_fwd_split(const void* q, const void* k, const void* v, void* o, float* 
 }
 
 size_t attn_decode_workspace_bytes(int B, int Hq, int d, int num_splits) {
-  if (B <= 0 || Hq <= 0 || d <= 0 || num_splits <= 0) return 0;
-  const size_t rows = (size_t)B * Hq * num_splits;
-  return round_up(rows * d * sizeof(float)) + round_up(rows * sizeof(float));
+  return decode_workspace_bytes(B, Hq, d, num_splits);
 }
 
 int attn_splitkv_combine(const float* o_part, const float* lse_part, void* o, float* lse, int B,
@@ -239,50 +345,17 @@ int attn_splitkv_combine(const float* o_part, const float* lse_part, void* o, fl
 int attn_fwd_decode(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                     int Hq, int Hkv, int Sk, int d, float scale, int dtype, int num_splits,
                     void* workspace, size_t workspace_bytes, void* stream) {
-  g_err[0] = '\0';
-  if (!q || !k || !v || !o)
-    return fail(ATTN_ERR_NULL, "attn_fwd_decode: q, k, v and o must be non-NULL");
-  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Sk <= 0 || d <= 0)
-    return fail(ATTN_ERR_SHAPE, "attn_fwd_decode: sizes must be positive");
-  if (Hq % Hkv != 0)
-    return fail(ATTN_ERR_SHAPE, "attn_fwd_decode: Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
-  if (dtype != ATTN_F16 && dtype != ATTN_BF16)
-    return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd_decode: dtype %d", dtype);
-  if (!attn::head_dim_supported(d))
-    return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd_decode: head dim %d (64 and 128 are implemented)",
-                d);
-  if (Hq / Hkv > 32)
-    return fail(ATTN_ERR_UNSUPPORTED, "attn_fwd_decode: query heads per kv head %d > 32",
-                Hq / Hkv);
-  if (num_splits < 1 || num_splits > Sk)
-    return fail(ATTN_ERR_VALUE, "attn_fwd_decode: num_splits=%d not in [1, Sk=%d]", num_splits, Sk);
-  if (!std::isfinite(scale) || scale < 0.0f)
-    return fail(ATTN_ERR_VALUE, "attn_fwd_decode: scale must be finite and >= 0");
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
-      (lse && !aligned4(lse)))
-    return fail(ATTN_ERR_ALIGN, "attn_fwd_decode: q, k, v, o must be 16-byte aligned, lse 4-byte");
-  const size_t need = attn_decode_workspace_bytes(B, Hq, d, num_splits);
-  if (!workspace || workspace_bytes < need)
-    return fail(ATTN_ERR_WORKSPACE, "attn_fwd_decode: workspace of %zu bytes needed, %zu given",
-                need, workspace ? workspace_bytes : (size_t)0);
-  if (!aligned16(workspace)) return fail(ATTN_ERR_ALIGN, "attn_fwd_decode: misaligned workspace");
-  if ((long long)B * Hkv * num_splits > INT_MAX || (long long)B * Hq > INT_MAX ||
-      (long long)B * Hkv * Sk * d > (1LL << 46))
-    return fail(ATTN_ERR_SHAPE, "attn_fwd_decode: problem too large for one launch");
-  if (Sk > kMaxSeq) return fail(ATTN_ERR_SHAPE, "attn_fwd_decode: Sk above %d", kMaxSeq);
-  int st = check_device();
-  if (st != ATTN_OK) return st;
-  const size_t rows = (size_t)B * Hq * num_splits;
-  float* o_part = static_cast<float*>(workspace);
-  float* lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                             round_up(rows * d * sizeof(float)));
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  attn::DecodeArgs da{q, k, v, o_part, lse_part, B, Hq, Hkv, Sk, d, num_splits,
-                      fold_log2e(scale), dtype};
-  st = hip_status(attn::launch_decode_split(da, s), "attn_fwd_decode split launch");
-  if (st != ATTN_OK) return st;
-  attn::CombineArgs ca{o_part, lse_part, o, lse, B * Hq, num_splits, d, dtype};
-  return hip_status(attn::launch_combine(ca, s), "attn_fwd_decode combine launch");
+  return decode("attn_fwd_decode", q, k, v, o, lse, B, Hq, Hkv, Sk, d, scale, dtype, num_splits,
+                workspace, workspace_bytes, stream, false);
 }
+
+int attn_fwd_decode_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int B, int Hq, int Hkv, int Sk, int d, float scale, int dtype,
+                            int num_splits, void* stream) {
+  return decode("attn_fwd_decode_noalloc", q, k, v, o, lse, B, Hq, Hkv, Sk, d, scale, dtype,
+                num_splits, nullptr, 0, stream, true);
+}
+
+size_t attn_decode_scratch_bytes(void) { return kScratchBytes; }
 
 }  // extern "C"

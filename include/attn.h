@@ -20,7 +20,8 @@
  * Layout.  Every tensor is contiguous row-major with d innermost:
  *     q, o: [B, Hq, Sq, d]      k, v: [B, Hkv, Sk, d]      lse: [B, Hq, Sq]
  * All data pointers are device pointers, 16-byte aligned, owned by the caller.
- * The library allocates nothing and keeps no state between calls.
+ * The library allocates nothing and keeps no state between calls; the one
+ * exception is attn_fwd_decode_noalloc's fixed per-GPU scratch (below).
  *
  * Streams.  Work is enqueued on `stream` (a hipStream_t; NULL = the default
  * stream) and the call returns before it completes.  Concurrent calls on
@@ -155,6 +156,28 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int d, int num_splits);
 int attn_fwd_decode(const void* q, const void* k, const void* v, void* o, float* lse,
                     int B, int Hq, int Hkv, int Sk, int d, float scale, int dtype,
                     int num_splits, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * attn_fwd_decode without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, serving loops and
+ * harnesses that forbid allocation.  The split partials go to a buffer the
+ * library owns, one fixed array of attn_decode_scratch_bytes() bytes (32 MiB)
+ * per GPU, held from the library's load until the process ends; nothing is
+ * allocated, on the device or the host, by this call.
+ *   Arguments, result and errors as attn_fwd_decode; ATTN_ERR_WORKSPACE when
+ *   attn_decode_workspace_bytes(B,Hq,d,num_splits) exceeds the scratch (the
+ *   64 x 32 x 16-split decode needs 16.9 MB of it).
+ * Every call on one GPU shares that GPU's scratch, and the buffer keeps the
+ * last call's partials: calls that overlap on one GPU (on different streams,
+ * or from several host threads without ordering) race and give wrong results.
+ * Serialise them, e.g. on one stream.
+ */
+int attn_fwd_decode_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int B, int Hq, int Hkv, int Sk, int d, float scale, int dtype,
+                            int num_splits, void* stream);
+
+/* Size in bytes of the per-GPU scratch attn_fwd_decode_noalloc uses. */
+size_t attn_decode_scratch_bytes(void);
 
 /*
  * Merge split partials: for each of the B*Hq rows,

@@ -199,3 +199,25 @@ def test_binding_rejects_host_tensors():
     q = torch.zeros(1, 1, 4, 128, dtype=torch.float16)
     with pytest.raises(A.AttnError):
         A.attn_fwd(q, q, q)
+
+
+@cpu_only
+def test_noalloc_decode_validation(L):
+    """The no-allocation decode validates as attn_fwd_decode does, and rejects
+    partials larger than its fixed scratch before any HIP call."""
+    def na(**kw):
+        a = dict(q=P, k=P, v=P, o=P, lse=None, B=2, Hq=8, Hkv=2, Sk=100, d=128, scale=0.1,
+                 dtype=1, ns=4)
+        a.update(kw)
+        return L.attn_fwd_decode_noalloc(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"],
+                                         a["Hq"], a["Hkv"], a["Sk"], a["d"], a["scale"],
+                                         a["dtype"], a["ns"], None)
+    assert A.attn_decode_scratch_bytes() == 32 << 20
+    assert na(q=None) == A.ATTN_ERR_NULL
+    assert na(Hq=7) == A.ATTN_ERR_SHAPE
+    assert na(ns=101) == A.ATTN_ERR_VALUE
+    assert na(d=96) == A.ATTN_ERR_UNSUPPORTED
+    # 64 x 64 rows x 32 splits x 128 fp32 = 64 MiB of partials > 32 MiB
+    assert na(B=64, Hq=64, Hkv=8, Sk=8192, ns=32) == A.ATTN_ERR_WORKSPACE
+    assert "scratch" in A.last_error()
+    assert na() == A.ATTN_ERR_NO_DEVICE
