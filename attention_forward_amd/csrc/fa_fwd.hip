@@ -24,6 +24,8 @@
 // test ("The FA5090 Optimization Journey", sec. 2.7 causal skip and sec. 2.8
 // mask specialisation).  Work items are issued heaviest first (largest query
 // block first), the LPT order of sec. 2.7.
+#include <atomic>
+
 #include "fa_common.h"
 #include "launch.h"
 
@@ -41,6 +43,17 @@ static_assert(KT == FWD_KT, "the host's split arithmetic uses the kernels' tile"
 // the 16-bit formats, whose MFMA phase is the long one, -0.2% at d = 128 and
 // -6% at d = 64, so they keep PV_FIRST.
 enum MfmaOrder { PV_FIRST = 0, QK_FIRST = 1 };
+
+// 1: persistent grid (one workgroup per compute unit, items in a snake
+// order); 0: one workgroup per item, dispatched by the hardware.
+#ifndef ATTN_PERSIST
+#define ATTN_PERSIST 1
+#endif
+// 1: an item's Q load and first K tile are issued together, then the
+// previous item's output stores, and one wait covers all three.
+#ifndef ATTN_OVERLAP
+#define ATTN_OVERLAP 1
+#endif
 #ifndef ATTN_ORDER16
 #define ATTN_ORDER16 0
 #endif
@@ -139,7 +152,8 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fa_fwd_kernel(
     const unsigned char* __restrict__ q, const unsigned char* __restrict__ k,
     const unsigned char* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse, int Hq,
     int Hkv, int Sq, int Sk_all, int causal, float scale_log2, float o_scale, int n_bh, int n_qt,
-    float* __restrict__ o_part, float* __restrict__ lse_part, int n_split, int split_keys) {
+    float* __restrict__ o_part, float* __restrict__ lse_part, int n_split, int split_keys,
+    int n_items) {
   constexpr int DT = F::DT, HD = F::HD;
   constexpr int NW = FWD_NW;
   constexpr int QB = 1;
@@ -161,304 +175,349 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fa_fwd_kernel(
   const int g = lane >> 5;
   const int n = lane & 31;
 
-  const int sp = PART ? (int)(blockIdx.x % (unsigned)n_split) : 0;
-  const int t = PART ? (int)(blockIdx.x / (unsigned)n_split) : (int)blockIdx.x;
-  const int rank = t / n_bh;
-  const int bh = t - rank * n_bh;
-  const int qt = causal ? (n_qt - 1 - rank) : rank;
-  const int b = bh / Hq;
-  const int hq = bh - b * Hq;
-  const int hkv = hq / (Hq / Hkv);
-
-  // keys [kv0, kv0 + Sk) of the head, indexed from kv0 below
-  const int kv0 = PART ? sp * split_keys : 0;
-  const int Sk = PART ? max(0, min(Sk_all - kv0, split_keys)) : Sk_all;
-  const unsigned char* qh = q + (size_t)bh * Sq * ROW;
-  const unsigned char* kh = k + (((size_t)b * Hkv + hkv) * Sk_all + kv0) * ROW;
-  const unsigned char* vh = v + (((size_t)b * Hkv + hkv) * Sk_all + kv0) * ROW;
-  // key i (from kv0) is visible to row r iff i <= r + causal_off
-  const int causal_off = Sk_all - Sq - kv0;
-
-  const int q0 = qt * BR;
-  const int qw0 = q0 + wave * 32;  // this wave's first query row
-
-  // keys this workgroup needs
-  int kv_end = Sk;
-  if (causal) {
-    const int last_q = min(q0 + BR, Sq) - 1;
-    kv_end = min(Sk, max(0, last_q + causal_off + 1));
-  }
-  const int n_tiles = (kv_end + KT - 1) / KT;
-  // tiles this wave computes: up to its own last visible key, none without rows
-  int n_wave = 0;
-  if (qw0 < Sq) {
-    const int wave_last_q = min(qw0 + 32, Sq) - 1;
-    const int wave_kv_end = causal ? min(Sk, max(0, wave_last_q + causal_off + 1)) : Sk;
-    n_wave = (wave_kv_end + KT - 1) / KT;
-  }
-
-  // Q^T operands of the wave's query n; rows past Sq read as zeros
-  typename F::QFrag qf;
-  {
-    const __amdgpu_buffer_rsrc_t qr = make_rsrc(qh, (long long)Sq * ROW);
-    F::load_q(qf, qr, (unsigned)((qw0 + n) * ROW));
-    vm_wait_all();  // Q is in registers before any tile load is issued
-  }
-
+  // Persistent: the grid has at most one workgroup per compute unit, and
+  // workgroup w takes items w, 2G - 1 - w, 2G + w, 4G - 1 - w, ... (G
+  // workgroups), a snake over the heaviest-first item order, so that with
+  // causal items (cost falling with the item index) every workgroup's total
+  // stays close to the mean.  Between items the workgroup keeps running:
+  // no dispatch gap, and the next item's loads start as soon as the last
+  // one's LDS reads are done (every wave has passed the final barrier).
   f32x16 acc[F::DBLOCKS][QB];
   float m[QB], l[QB];
-  m[0] = -INFINITY;
-  l[0] = 0.0f;
+  // epilogue of an item: O = acc / l, rounded to the dtype; LSE = ln2 * (m + log2 l)
+  auto epilogue = [&](int bh, int qw0, int sp) {
+    if constexpr (PART) {
+      const float lt = half_sum(l[0]);
+      const float inv = lt > 0.0f ? o_scale / lt : 0.0f;
+      const int row = qw0 + n;
+      if (row < Sq) {
+        const size_t prow = ((size_t)bh * Sq + row) * n_split + sp;
+        float* orow = o_part + prow * D;
 #pragma unroll
-  for (int db = 0; db < F::DBLOCKS; ++db) acc[db][0] = f32x16{};
-
-  // The loading waves split every tile: with L of them, chunk L*c + w covers
-  // rows 4(L*c + w) + lane/16 (w = the wave's index among the loaders); L*c*4
-  // is a multiple of 16 rows, so one swizzle pattern (and one lane offset)
-  // serves all of a wave's chunks
-  constexpr int LOADERS = LM >= 2 ? NW : NW / 2;
-  constexpr int CHUNKS_PER_LOADER = G::CHUNKS / LOADERS;
-  static_assert(CHUNKS_PER_LOADER * LOADERS == G::CHUNKS && (LOADERS * G::RPC) % 16 == 0,
-                "whole chunks per loader, 16-row strides");
-  const unsigned koff = F::template load_offset<false>(wave & (LOADERS - 1));
-  const unsigned voff = F::template load_offset<true>(wave & (LOADERS - 1));
-  unsigned char ATTN_LDS* lds = (unsigned char ATTN_LDS*)(smem);
-  auto issue = [&](const unsigned char* head, unsigned lane_off, int j,
-                   unsigned char ATTN_LDS* dst) {
-    const int key0 = j * KT;
-    // keys past Sk read as zeros
-    const __amdgpu_buffer_rsrc_t r =
-        make_rsrc(head + (size_t)key0 * ROW, (long long)(Sk - key0) * ROW);
+        for (int db = 0; db < F::DBLOCKS; ++db)
 #pragma unroll
-    for (int c = 0; c < CHUNKS_PER_LOADER; ++c)
-      load_chunk(r, lane_off + c * LOADERS * 1024,
-                 dst + (c * LOADERS + (wave & (LOADERS - 1))) * 1024);
-  };
-  auto stage = [](int j) { return ST == 2 ? (j & 1) : j % ST; };
-  auto k_stage = [&](int j) { return lds + stage(j) * TILE_BYTES; };
-  auto v_stage = [&](int j) { return lds + (ST + stage(j)) * TILE_BYTES; };
-  const LaneAddr la = F::lanes();
-  const unsigned lds_base = (unsigned)(size_t)lds;
-
-  f32x16 s[2][QB];
-  typename F::PFrag pf;
-
-  // Every wave runs the same sequence  [MFMA(j)] barrier [softmax(j)] barrier,
-  // group B one barrier later than group A, so each half-step pairs A's MFMA
-  // phase with B's softmax phase and vice versa.  Group A issues K(j+1) and
-  // V(j) at the start of its step j and waits for them at its end: their
-  // stages were last read by B's MFMA phase of step j-1, which ends before the
-  // barrier A passes to start step j, and they are next read by A's MFMA phase
-  // of step j+1.
-  // The loads of step j, K(j+1) and V(j), are issued at the start of the
-  // half-step in which A runs its MFMA phase j, and have landed by the end of
-  // the next one.  A issues its share at the start of its MFMA phase and waits
-  // at the end of its softmax phase; B issues its share at the start of its
-  // softmax phase (of step j-1) and waits at the end of its MFMA phase j.
-  // Either way the stages written are free (last read before the barrier that
-  // opens the half-step) and are next read after the barrier that closes the
-  // wait.  ATTN_LOADERS: 0 = A loads everything, 1 = B does, 2 = both halves
-  // (the issue of direct-to-LDS loads holds up the issuing wave for a while,
-  // so the cost is best split between the two phases of the half-step).
-  // ATTN_LOADERS 3 (with three stages per ring): both groups issue half of
-  // step j+1's loads, K(j+2) and V(j+1), at the start of their softmax phase
-  // j, and wait for them at the end of their next MFMA phase.  A's softmax
-  // phase j runs beside B's MFMA phase j, which reads K(j) and V(j-1); the
-  // stages written held K(j-1) and V(j-2), last read in MFMA phase j-1.  So
-  // each softmax phase carries half the issue cost, and the DMA writes into
-  // LDS land half beside each group's MFMA phase.
-  constexpr bool SOFTMAX_LOADS = LM == 3;
-  constexpr bool A_LOADS = LM != 1, B_LOADS = LM != 0;
-  const bool loader = group_a ? A_LOADS : B_LOADS;
-  auto issue_step = [&](int j) {
-    if (j + 1 < n_tiles) issue(kh, koff, j + 1, k_stage(j + 1));
-    if (j < n_tiles) issue(vh, voff, j, v_stage(j));
-  };
-  auto mfma_begin = [&](int j) {
-    if (A_LOADS && !SOFTMAX_LOADS && group_a) issue_step(j);
-  };
-  auto mfma_end = [&]() {
-    if (SOFTMAX_LOADS || (B_LOADS && !group_a)) vm_wait_all();
-  };
-  auto softmax_begin = [&](int j) {
-    if (SOFTMAX_LOADS || (B_LOADS && !group_a)) issue_step(j + 1);
-  };
-  auto softmax_end = [&]() {
-    if (A_LOADS && !SOFTMAX_LOADS && group_a) vm_wait_all();
-  };
-  auto barrier = [] { __builtin_amdgcn_s_barrier(); };
-  auto k_addr = [&](int j) { return lds_base + (unsigned)(stage(j) * TILE_BYTES); };
-  auto v_addr = [&](int j) { return lds_base + (unsigned)((ST + stage(j)) * TILE_BYTES); };
-  float alpha[QB];
-  auto masked = [&](int j) {
-    const int key0 = j * KT;
-    return (key0 + KT > Sk) || (causal && key0 + KT - 1 > qw0 + causal_off);
-  };
-  // online softmax of tile j without touching O: returns whether some lane's
-  // finite reference max moved, i.e. whether O must still be scaled by alpha
-  auto softmax_keep_o = [&](int j) {
-    const int key0 = j * KT;
-    if (masked(j))
-      return softmax_step<DT, QB, true, false>(s, acc, m, l, pf, scale_log2, key0, qw0, Sk,
-                                               causal != 0, causal_off, alpha);
-    // the max-free form rests on the threshold rule, which FP8 does not use
-    if (ATTN_FAST_SOFTMAX && !F::FP8 && !softmax_fast<DT, QB>(s, m, l, pf, scale_log2))
-      return false;
-    return softmax_step<DT, QB, false, false>(s, acc, m, l, pf, scale_log2, key0, qw0, Sk,
-                                              false, 0, alpha);
-  };
-  // the same with O scaled by alpha
-  auto softmax_scale_o = [&](int j) {
-    const int key0 = j * KT;
-    if (masked(j))
-      softmax_step<DT, QB, true>(s, acc, m, l, pf, scale_log2, key0, qw0, Sk, causal != 0,
-                                 causal_off, alpha);
-    else
-      softmax_step<DT, QB, false>(s, acc, m, l, pf, scale_log2, key0, qw0, Sk, false, 0, alpha);
-  };
-  auto prio_hi = [] {
-    if (ATTN_SETPRIO) __builtin_amdgcn_s_setprio(1);
-  };
-  auto prio_lo = [] {
-    if (ATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
-  };
-
-  if (loader && n_tiles > 0) issue(kh, koff, 0, k_stage(0));
-  vm_wait_all();
-  // A's half of step 0 (K(1), V(0)), waited at the end of its first MFMA phase
-  if (SOFTMAX_LOADS && group_a) issue_step(0);
-  barrier();
-  if (!group_a) {
-    softmax_begin(-1);  // the half-step before B's first MFMA phase
-    barrier();
-  }
-  // The loop is peeled at this wave's first and last computed tile, and the
-  // middle runs in two loops, so that inside each loop the accumulator is
-  // updated unconditionally (a path that skips an update makes the register
-  // allocator copy the accumulator on every iteration).  The first loop never
-  // scales O: with the threshold rule alpha is exactly 1 until some lane's
-  // finite reference max moves, which for most rows never happens after their
-  // first tile.  When it does, O is scaled once and the rest of the tiles run
-  // in the second loop, which scales O on every tile as the recurrence is
-  // written.  The first tile needs no scaling: O is still zero.  (With the
-  // exact running max of FP8, a wave usually reaches the second loop within
-  // its first few tiles.)
-  // MFMA phase of step j, 0 < j < n_wave, in the format's order
-  auto mfma_phase = [&](int j) {
-    if constexpr (F::ORDER == QK_FIRST) {
-      F::qk(k_addr(j), la, qf, s);
-      F::pv(v_addr(j - 1), la, pf, acc);
+          for (int jj = 0; jj < 4; ++jj) {
+            const int d0 = 32 * db + 8 * jj + 4 * g;
+            f32x4 w;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w[e] = acc[db][0][4 * jj + e] * inv;
+            *reinterpret_cast<f32x4*>(orow + d0) = w;
+          }
+        if (g == 0)
+          lse_part[prow] =
+              lt > 0.0f ? 0.69314718055994531f * (m[0] + __builtin_amdgcn_logf(lt)) : -INFINITY;
+      }
     } else {
-      F::pv(v_addr(j - 1), la, pf, acc);
-      F::qk(k_addr(j), la, qf, s);
-    }
-  };
-  int j = 0;
-  if (n_wave > 0) {
-    mfma_begin(0);
-    prio_hi();
-    F::qk(k_addr(0), la, qf, s);
-    prio_lo();
-    mfma_end();
-    barrier();
-    softmax_begin(0);
-    softmax_keep_o(0);
-    softmax_end();
-    barrier();
-    for (j = 1; j < n_wave; ++j) {
-      mfma_begin(j);
-      prio_hi();
-      mfma_phase(j);
-      prio_lo();
-      mfma_end();
-      barrier();
-      softmax_begin(j);
-      const bool moved = softmax_keep_o(j);
-      softmax_end();
-      barrier();
-      if (moved) {
+      const float lt = half_sum(l[0]);
+      const float inv = lt > 0.0f ? o_scale / lt : 0.0f;
+      const int row = qw0 + n;
+      if (row < Sq) {
+        uint16_t* orow = o + ((size_t)bh * Sq + row) * D;
 #pragma unroll
-        for (int db = 0; db < F::DBLOCKS; ++db) acc[db][0] *= alpha[0];
-        ++j;
-        break;
+        for (int db = 0; db < F::DBLOCKS; ++db)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const int d0 = 32 * db + 8 * jj + 4 * g;
+            u32x2 w;
+            w[0] = pack2<DT>(acc[db][0][4 * jj + 0] * inv, acc[db][0][4 * jj + 1] * inv);
+            w[1] = pack2<DT>(acc[db][0][4 * jj + 2] * inv, acc[db][0][4 * jj + 3] * inv);
+            *reinterpret_cast<u32x2*>(orow + d0) = w;
+          }
+        if (lse != nullptr && g == 0)
+          lse[(size_t)bh * Sq + row] =
+              lt > 0.0f ? 0.69314718055994531f * (m[0] + __builtin_amdgcn_logf(lt)) : -INFINITY;
       }
     }
-    for (; j < n_wave; ++j) {
+  };
+  // the item whose output is still to be written (ATTN_OVERLAP: the stores of
+  // one item are issued after the next item's first loads, so that their
+  // latencies overlap)
+  bool pending = false;
+  int p_bh = 0, p_qw0 = 0, p_sp = 0;
+
+  const int n_wg = (int)gridDim.x;
+  for (int round = 0;; ++round) {
+    const int item = round * n_wg + ((round & 1) ? n_wg - 1 - (int)blockIdx.x : (int)blockIdx.x);
+    if (item >= n_items) break;
+    const int sp = PART ? item % n_split : 0;
+    const int t = PART ? item / n_split : item;
+    const int rank = t / n_bh;
+    const int bh = t - rank * n_bh;
+    const int qt = causal ? (n_qt - 1 - rank) : rank;
+    const int b = bh / Hq;
+    const int hq = bh - b * Hq;
+    const int hkv = hq / (Hq / Hkv);
+
+    // keys [kv0, kv0 + Sk) of the head, indexed from kv0 below
+    const int kv0 = PART ? sp * split_keys : 0;
+    const int Sk = PART ? max(0, min(Sk_all - kv0, split_keys)) : Sk_all;
+    const unsigned char* qh = q + (size_t)bh * Sq * ROW;
+    const unsigned char* kh = k + (((size_t)b * Hkv + hkv) * Sk_all + kv0) * ROW;
+    const unsigned char* vh = v + (((size_t)b * Hkv + hkv) * Sk_all + kv0) * ROW;
+    // key i (from kv0) is visible to row r iff i <= r + causal_off
+    const int causal_off = Sk_all - Sq - kv0;
+
+    const int q0 = qt * BR;
+    const int qw0 = q0 + wave * 32;  // this wave's first query row
+
+    // keys this workgroup needs
+    int kv_end = Sk;
+    if (causal) {
+      const int last_q = min(q0 + BR, Sq) - 1;
+      kv_end = min(Sk, max(0, last_q + causal_off + 1));
+    }
+    const int n_tiles = (kv_end + KT - 1) / KT;
+    // tiles this wave computes: up to its own last visible key, none without rows
+    int n_wave = 0;
+    if (qw0 < Sq) {
+      const int wave_last_q = min(qw0 + 32, Sq) - 1;
+      const int wave_kv_end = causal ? min(Sk, max(0, wave_last_q + causal_off + 1)) : Sk;
+      n_wave = (wave_kv_end + KT - 1) / KT;
+    }
+
+    // Q^T operands of the wave's query n; rows past Sq read as zeros
+    typename F::QFrag qf;
+    {
+      const __amdgpu_buffer_rsrc_t qr = make_rsrc(qh, (long long)Sq * ROW);
+      F::load_q(qf, qr, (unsigned)((qw0 + n) * ROW));
+      if (!ATTN_OVERLAP) vm_wait_all();  // Q is in registers before any tile load is issued
+    }
+
+    // The loading waves split every tile: with L of them, chunk L*c + w covers
+    // rows 4(L*c + w) + lane/16 (w = the wave's index among the loaders); L*c*4
+    // is a multiple of 16 rows, so one swizzle pattern (and one lane offset)
+    // serves all of a wave's chunks
+    constexpr int LOADERS = LM >= 2 ? NW : NW / 2;
+    constexpr int CHUNKS_PER_LOADER = G::CHUNKS / LOADERS;
+    static_assert(CHUNKS_PER_LOADER * LOADERS == G::CHUNKS && (LOADERS * G::RPC) % 16 == 0,
+                  "whole chunks per loader, 16-row strides");
+    const unsigned koff = F::template load_offset<false>(wave & (LOADERS - 1));
+    const unsigned voff = F::template load_offset<true>(wave & (LOADERS - 1));
+    unsigned char ATTN_LDS* lds = (unsigned char ATTN_LDS*)(smem);
+    auto issue = [&](const unsigned char* head, unsigned lane_off, int j,
+                     unsigned char ATTN_LDS* dst) {
+      const int key0 = j * KT;
+      // keys past Sk read as zeros
+      const __amdgpu_buffer_rsrc_t r =
+          make_rsrc(head + (size_t)key0 * ROW, (long long)(Sk - key0) * ROW);
+#pragma unroll
+      for (int c = 0; c < CHUNKS_PER_LOADER; ++c)
+        load_chunk(r, lane_off + c * LOADERS * 1024,
+                   dst + (c * LOADERS + (wave & (LOADERS - 1))) * 1024);
+    };
+    auto stage = [](int j) { return ST == 2 ? (j & 1) : j % ST; };
+    auto k_stage = [&](int j) { return lds + stage(j) * TILE_BYTES; };
+    auto v_stage = [&](int j) { return lds + (ST + stage(j)) * TILE_BYTES; };
+    const LaneAddr la = F::lanes();
+    const unsigned lds_base = (unsigned)(size_t)lds;
+
+    f32x16 s[2][QB];
+    typename F::PFrag pf;
+
+    // Every wave runs the same sequence  [MFMA(j)] barrier [softmax(j)] barrier,
+    // group B one barrier later than group A, so each half-step pairs A's MFMA
+    // phase with B's softmax phase and vice versa.  Group A issues K(j+1) and
+    // V(j) at the start of its step j and waits for them at its end: their
+    // stages were last read by B's MFMA phase of step j-1, which ends before the
+    // barrier A passes to start step j, and they are next read by A's MFMA phase
+    // of step j+1.
+    // The loads of step j, K(j+1) and V(j), are issued at the start of the
+    // half-step in which A runs its MFMA phase j, and have landed by the end of
+    // the next one.  A issues its share at the start of its MFMA phase and waits
+    // at the end of its softmax phase; B issues its share at the start of its
+    // softmax phase (of step j-1) and waits at the end of its MFMA phase j.
+    // Either way the stages written are free (last read before the barrier that
+    // opens the half-step) and are next read after the barrier that closes the
+    // wait.  ATTN_LOADERS: 0 = A loads everything, 1 = B does, 2 = both halves
+    // (the issue of direct-to-LDS loads holds up the issuing wave for a while,
+    // so the cost is best split between the two phases of the half-step).
+    // ATTN_LOADERS 3 (with three stages per ring): both groups issue half of
+    // step j+1's loads, K(j+2) and V(j+1), at the start of their softmax phase
+    // j, and wait for them at the end of their next MFMA phase.  A's softmax
+    // phase j runs beside B's MFMA phase j, which reads K(j) and V(j-1); the
+    // stages written held K(j-1) and V(j-2), last read in MFMA phase j-1.  So
+    // each softmax phase carries half the issue cost, and the DMA writes into
+    // LDS land half beside each group's MFMA phase.
+    constexpr bool SOFTMAX_LOADS = LM == 3;
+    constexpr bool A_LOADS = LM != 1, B_LOADS = LM != 0;
+    const bool loader = group_a ? A_LOADS : B_LOADS;
+    auto issue_step = [&](int j) {
+      if (j + 1 < n_tiles) issue(kh, koff, j + 1, k_stage(j + 1));
+      if (j < n_tiles) issue(vh, voff, j, v_stage(j));
+    };
+    auto mfma_begin = [&](int j) {
+      if (A_LOADS && !SOFTMAX_LOADS && group_a) issue_step(j);
+    };
+    auto mfma_end = [&]() {
+      if (SOFTMAX_LOADS || (B_LOADS && !group_a)) vm_wait_all();
+    };
+    auto softmax_begin = [&](int j) {
+      if (SOFTMAX_LOADS || (B_LOADS && !group_a)) issue_step(j + 1);
+    };
+    auto softmax_end = [&]() {
+      if (A_LOADS && !SOFTMAX_LOADS && group_a) vm_wait_all();
+    };
+    auto barrier = [] { __builtin_amdgcn_s_barrier(); };
+    auto k_addr = [&](int j) { return lds_base + (unsigned)(stage(j) * TILE_BYTES); };
+    auto v_addr = [&](int j) { return lds_base + (unsigned)((ST + stage(j)) * TILE_BYTES); };
+    float alpha[QB];
+    auto masked = [&](int j) {
+      const int key0 = j * KT;
+      return (key0 + KT > Sk) || (causal && key0 + KT - 1 > qw0 + causal_off);
+    };
+    // online softmax of tile j without touching O: returns whether some lane's
+    // finite reference max moved, i.e. whether O must still be scaled by alpha
+    auto softmax_keep_o = [&](int j) {
+      const int key0 = j * KT;
+      if (masked(j))
+        return softmax_step<DT, QB, true, false>(s, acc, m, l, pf, scale_log2, key0, qw0, Sk,
+                                                 causal != 0, causal_off, alpha);
+      // the max-free form rests on the threshold rule, which FP8 does not use
+      if (ATTN_FAST_SOFTMAX && !F::FP8 && !softmax_fast<DT, QB>(s, m, l, pf, scale_log2))
+        return false;
+      return softmax_step<DT, QB, false, false>(s, acc, m, l, pf, scale_log2, key0, qw0, Sk,
+                                                false, 0, alpha);
+    };
+    // the same with O scaled by alpha
+    auto softmax_scale_o = [&](int j) {
+      const int key0 = j * KT;
+      if (masked(j))
+        softmax_step<DT, QB, true>(s, acc, m, l, pf, scale_log2, key0, qw0, Sk, causal != 0,
+                                   causal_off, alpha);
+      else
+        softmax_step<DT, QB, false>(s, acc, m, l, pf, scale_log2, key0, qw0, Sk, false, 0, alpha);
+    };
+    auto prio_hi = [] {
+      if (ATTN_SETPRIO) __builtin_amdgcn_s_setprio(1);
+    };
+    auto prio_lo = [] {
+      if (ATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
+    };
+
+    if (loader && n_tiles > 0) issue(kh, koff, 0, k_stage(0));
+    if (ATTN_OVERLAP && pending) epilogue(p_bh, p_qw0, p_sp);
+    vm_wait_all();
+    m[0] = -INFINITY;
+    l[0] = 0.0f;
+#pragma unroll
+    for (int db = 0; db < F::DBLOCKS; ++db) acc[db][0] = f32x16{};
+    // A's half of step 0 (K(1), V(0)), waited at the end of its first MFMA phase
+    if (SOFTMAX_LOADS && group_a) issue_step(0);
+    barrier();
+    if (!group_a) {
+      softmax_begin(-1);  // the half-step before B's first MFMA phase
+      barrier();
+    }
+    // The loop is peeled at this wave's first and last computed tile, and the
+    // middle runs in two loops, so that inside each loop the accumulator is
+    // updated unconditionally (a path that skips an update makes the register
+    // allocator copy the accumulator on every iteration).  The first loop never
+    // scales O: with the threshold rule alpha is exactly 1 until some lane's
+    // finite reference max moves, which for most rows never happens after their
+    // first tile.  When it does, O is scaled once and the rest of the tiles run
+    // in the second loop, which scales O on every tile as the recurrence is
+    // written.  The first tile needs no scaling: O is still zero.  (With the
+    // exact running max of FP8, a wave usually reaches the second loop within
+    // its first few tiles.)
+    // MFMA phase of step j, 0 < j < n_wave, in the format's order
+    auto mfma_phase = [&](int j) {
+      if constexpr (F::ORDER == QK_FIRST) {
+        F::qk(k_addr(j), la, qf, s);
+        F::pv(v_addr(j - 1), la, pf, acc);
+      } else {
+        F::pv(v_addr(j - 1), la, pf, acc);
+        F::qk(k_addr(j), la, qf, s);
+      }
+    };
+    int j = 0;
+    if (n_wave > 0) {
+      mfma_begin(0);
+      prio_hi();
+      F::qk(k_addr(0), la, qf, s);
+      prio_lo();
+      mfma_end();
+      barrier();
+      softmax_begin(0);
+      softmax_keep_o(0);
+      softmax_end();
+      barrier();
+      for (j = 1; j < n_wave; ++j) {
+        mfma_begin(j);
+        prio_hi();
+        mfma_phase(j);
+        prio_lo();
+        mfma_end();
+        barrier();
+        softmax_begin(j);
+        const bool moved = softmax_keep_o(j);
+        softmax_end();
+        barrier();
+        if (moved) {
+#pragma unroll
+          for (int db = 0; db < F::DBLOCKS; ++db) acc[db][0] *= alpha[0];
+          ++j;
+          break;
+        }
+      }
+      for (; j < n_wave; ++j) {
+        mfma_begin(j);
+        prio_hi();
+        mfma_phase(j);
+        prio_lo();
+        mfma_end();
+        barrier();
+        softmax_begin(j);
+        softmax_scale_o(j);
+        softmax_end();
+        barrier();
+      }
       mfma_begin(j);
       prio_hi();
-      mfma_phase(j);
+      F::pv(v_addr(j - 1), la, pf, acc);
       prio_lo();
       mfma_end();
       barrier();
       softmax_begin(j);
-      softmax_scale_o(j);
+      softmax_end();
+      barrier();
+      ++j;
+    }
+    for (; j <= n_tiles; ++j) {  // steps with nothing left for this wave
+      mfma_begin(j);
+      mfma_end();
+      barrier();
+      softmax_begin(j);
       softmax_end();
       barrier();
     }
-    mfma_begin(j);
-    prio_hi();
-    F::pv(v_addr(j - 1), la, pf, acc);
-    prio_lo();
-    mfma_end();
-    barrier();
-    softmax_begin(j);
-    softmax_end();
-    barrier();
-    ++j;
-  }
-  for (; j <= n_tiles; ++j) {  // steps with nothing left for this wave
-    mfma_begin(j);
-    mfma_end();
-    barrier();
-    softmax_begin(j);
-    softmax_end();
-    barrier();
-  }
-  if (group_a) barrier();
+    if (group_a) barrier();
 
-  // epilogue: O = acc / l, rounded to the dtype; LSE = ln2 * (m + log2 l)
-  if constexpr (PART) {
-    const float lt = half_sum(l[0]);
-    const float inv = lt > 0.0f ? o_scale / lt : 0.0f;
-    const int row = qw0 + n;
-    if (row < Sq) {
-      const size_t prow = ((size_t)bh * Sq + row) * n_split + sp;
-      float* orow = o_part + prow * D;
-#pragma unroll
-      for (int db = 0; db < F::DBLOCKS; ++db)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int d0 = 32 * db + 8 * jj + 4 * g;
-          f32x4 w;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = acc[db][0][4 * jj + e] * inv;
-          *reinterpret_cast<f32x4*>(orow + d0) = w;
-        }
-      if (g == 0)
-        lse_part[prow] =
-            lt > 0.0f ? 0.69314718055994531f * (m[0] + __builtin_amdgcn_logf(lt)) : -INFINITY;
-    }
-  } else {
-    const float lt = half_sum(l[0]);
-    const float inv = lt > 0.0f ? o_scale / lt : 0.0f;
-    const int row = qw0 + n;
-    if (row < Sq) {
-      uint16_t* orow = o + ((size_t)bh * Sq + row) * D;
-#pragma unroll
-      for (int db = 0; db < F::DBLOCKS; ++db)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int d0 = 32 * db + 8 * jj + 4 * g;
-          u32x2 w;
-          w[0] = pack2<DT>(acc[db][0][4 * jj + 0] * inv, acc[db][0][4 * jj + 1] * inv);
-          w[1] = pack2<DT>(acc[db][0][4 * jj + 2] * inv, acc[db][0][4 * jj + 3] * inv);
-          *reinterpret_cast<u32x2*>(orow + d0) = w;
-        }
-      if (lse != nullptr && g == 0)
-        lse[(size_t)bh * Sq + row] =
-            lt > 0.0f ? 0.69314718055994531f * (m[0] + __builtin_amdgcn_logf(lt)) : -INFINITY;
+    if (ATTN_OVERLAP) {
+      pending = true;
+      p_bh = bh;
+      p_qw0 = qw0;
+      p_sp = sp;
+    } else {
+      epilogue(bh, qw0, sp);
     }
   }
+  if (pending) epilogue(p_bh, p_qw0, p_sp);
+}
+
+// Compute units of the device `stream` runs on (0 if unknown), cached per device.
+static int compute_units(hipStream_t stream) {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if ((stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev)) != hipSuccess || dev < 0 ||
+      dev >= 64)
+    return 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
 }
 
 template <typename F, bool PART>
@@ -467,13 +526,14 @@ static void launch_fwd_t(const FwdArgs& a, const FwdSplitArgs* sa, hipStream_t s
   const int n_qt = (a.Sq + FWD_BR - 1) / FWD_BR;
   const int n_split = PART ? sa->num_splits : 1;
   const long long items = (long long)n_bh * n_qt * n_split;
-  dim3 grid((unsigned)items), block(FWD_NW * 64);
+  const int cus = ATTN_PERSIST ? compute_units(stream) : 0;
+  dim3 grid((unsigned)(cus > 0 && items > cus ? cus : items)), block(FWD_NW * 64);
   hipLaunchKernelGGL((fa_fwd_kernel<F, PART>), grid, block, 0, stream,
                      static_cast<const unsigned char*>(a.q), static_cast<const unsigned char*>(a.k),
                      static_cast<const unsigned char*>(a.v), static_cast<uint16_t*>(a.o), a.lse,
                      a.Hq, a.Hkv, a.Sq, a.Sk, a.causal, a.scale_log2, a.o_scale, n_bh, n_qt,
                      PART ? sa->o_part : nullptr, PART ? sa->lse_part : nullptr, n_split,
-                     PART ? sa->split_keys : 0);
+                     PART ? sa->split_keys : 0, (int)items);
 }
 
 template <bool PART>
