@@ -108,13 +108,17 @@ def _time_ms(fn, iters, warmup=3):
     return s.elapsed_time(e) / iters
 
 
-def _time_ms_median(fn, iters, warmup=3, rounds=5, rest_s=0.5):
-    """Median over `rounds` of _time_ms, after a short rest so that the clock
-    recovers from the workloads timed before (the context figures follow the
-    sustained headline steps and the GEMM ceilings)."""
-    torch.cuda.synchronize()
-    time.sleep(rest_s)
-    ts = sorted(_time_ms(fn, iters, warmup if r == 0 else 1) for r in range(rounds))
+def _time_ms_median(fn, iters, warm_s=0.75, rounds=5):
+    """Median over `rounds` of _time_ms, after at least warm_s seconds of the same
+    launches: the engine clock rises under sustained load and settles within
+    about a second, so each figure is taken in the loaded state, as the
+    headline steps are."""
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < warm_s:
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
+    ts = sorted(_time_ms(fn, iters, 1) for r in range(rounds))
     return ts[len(ts) // 2]
 
 
@@ -170,14 +174,14 @@ def other_workloads(iters=20):
             ws = torch.empty(A.attn_decode_workspace_bytes(w.B, w.Hq, w.d, w.num_splits),
                              device="cuda", dtype=torch.uint8)
             ms = _time_ms_median(lambda: A.attn_fwd_decode(q, k, v, w.num_splits, scale=w.scale, out=o,
-                                                    lse=lse, workspace=ws), iters, warmup=10)
+                                                    lse=lse, workspace=ws), iters)
             out[name] = {"ms": round(ms, 4),
                          "gbs": round(decode_algorithmic_bytes(w) / (ms * 1e-3) / 1e9, 1)}
             del ws
         else:
             lse = torch.empty(q.shape[:3], device="cuda", dtype=torch.float32)
             ms = _time_ms_median(lambda: A.attn_fwd(q, k, v, causal=w.causal, scale=w.scale, out=o,
-                                             lse=lse), iters, warmup=10)
+                                             lse=lse), iters)
             out[name] = {"ms": round(ms, 4), "tflops": round(w.flops / (ms * 1e-3) / 1e12, 2)}
             # under-filled grids: the split-KV form with the recommended split count
             ns = A.attn_fwd_num_splits(w.B, w.Hq, w.Sq, w.Sk, w.d)
@@ -186,7 +190,7 @@ def other_workloads(iters=20):
                                  device="cuda", dtype=torch.uint8)
                 ms = _time_ms_median(lambda: A.attn_fwd_split(q, k, v, ns, causal=w.causal,
                                                        scale=w.scale, out=o, lse=lse,
-                                                       workspace=ws), iters, warmup=10)
+                                                       workspace=ws), iters)
                 out[name]["split"] = {"num_splits": ns, "ms": round(ms, 4),
                                       "tflops": round(w.flops / (ms * 1e-3) / 1e12, 2)}
                 del ws
@@ -198,7 +202,7 @@ def other_workloads(iters=20):
         lse = torch.empty((w.B, w.Hq, w.Sq), device="cuda", dtype=torch.float32)
         ms = _time_ms_median(lambda: A.attn_fwd_fp8(q, k, v, causal=w.causal, scale=w.scale,
                                              q_descale=ds[0], k_descale=ds[1], v_descale=ds[2],
-                                             out=o, lse=lse), iters, warmup=10)
+                                             out=o, lse=lse), iters)
         tf = w.flops / (ms * 1e-3) / 1e12
         out[name] = {"ms": round(ms, 4), "tflops": round(tf, 2),
                      "frac_fp8_mfma_peak": round(tf / FP8_PEAK_TFLOPS, 4)}
