@@ -193,6 +193,11 @@ __device__ __forceinline__ u32x4 load_b128(__amdgpu_buffer_rsrc_t r, unsigned vo
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0));
 }
 
+// 16 bytes per lane to rsrc at byte offset voff; offsets past the range are dropped
+__device__ __forceinline__ void store_b128(__amdgpu_buffer_rsrc_t r, unsigned voff, u32x4 x) {
+  __builtin_amdgcn_raw_buffer_store_b128(x, r, (int)voff, 0, 0);
+}
+
 // s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in bits
 // 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).  Issued
 // through the builtin so the compiler's own wait bookkeeping sees it.
@@ -224,6 +229,11 @@ template <int N>
 __device__ __forceinline__ void lgkm_wait(u32x4& x) {
   asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(x) : "n"(N));
 }
+__device__ __forceinline__ void lds_write_b64(unsigned addr, u32x2 x) {
+  asm volatile("ds_write_b64 %0, %1" : : "v"(addr), "v"(x) : "memory");
+}
+// every LDS access issued so far has completed
+__device__ __forceinline__ void lgkm_drain() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 // Per-lane LDS byte addresses (relative to a K/V stage) that stay fixed for
 // the whole key loop; tile, stage and step offsets are immediates.  Entries
@@ -232,6 +242,37 @@ struct LaneAddr {
   unsigned k[8];  // K operand of d-step st (key block 0; block 1 is +32 rows)
   unsigned v[4];  // V^T operand of d-block db (key step 0; others are row offsets)
 };
+// The swizzles only permute 16-byte slots within a row, and the slot index of
+// d-step st (d-block db) differs from that of d-step 0 (d-block 0) in the bits
+// that st (db) XORs in: k[st] = k[0] ^ (st << 5), and v[db] = v[0] ^ (db <<
+// VSH) with VSH 6 for the 16-bit layouts (4 slots per d-block) and 5 for FP8
+// (2 slots).  Stage bases are multiples of 1 KiB, so the XOR commutes with
+// adding the stage base: with ATTN_COMPACT_LA the kernels keep only k[0] and
+// v[0] in registers and form the others with one XOR per read, in place of
+// the add of the base they need anyway.
+#ifndef ATTN_COMPACT_LA
+#define ATTN_COMPACT_LA 1
+#endif
+// k0 / v0: base + k[0] (base + v[0]) formed once per tile step; the empty asm
+// makes it opaque, so that the compiler cannot fold the XOR constants into
+// the lane address and keep every d-step's address in a register again.
+// COMPACT selects the form per caller: the 16-bit steps use it (ATTN_COMPACT_LA),
+// the FP8 steps keep every address in a register (the compact form measured
+// 1.3% slower there).
+template <bool COMPACT = ATTN_COMPACT_LA>
+__device__ __forceinline__ unsigned lane_base(unsigned base, unsigned lane_addr) {
+  unsigned a = base + lane_addr;
+  if (COMPACT) asm volatile("" : "+v"(a));
+  return a;
+}
+template <bool COMPACT = ATTN_COMPACT_LA>
+__device__ __forceinline__ unsigned kaddr(unsigned k0, const LaneAddr& la, unsigned base, int st) {
+  return COMPACT ? (k0 ^ (unsigned)(st << 5)) : base + la.k[st];
+}
+template <int VSH, bool COMPACT = ATTN_COMPACT_LA>
+__device__ __forceinline__ unsigned vaddr(unsigned v0, const LaneAddr& la, unsigned base, int db) {
+  return COMPACT ? (v0 ^ (unsigned)(db << VSH)) : base + la.v[db];
+}
 
 template <int HD>
 __device__ __forceinline__ LaneAddr lane_addresses() {
@@ -325,16 +366,17 @@ template <int QB>
 __device__ __forceinline__ void qk_step8(unsigned kbase, const LaneAddr& la,
                                          const u32x8 (&qf)[QB][2], f32x16 (&s)[2][QB]) {
   u32x8 ko[4];
+  const unsigned k0 = lane_base<false>(kbase, la.k[0]);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int kb = i >> 1, st = i & 1;
     u32x4 lo, hi;
     if (kb == 0) {
-      lo = lds_b128<0>(kbase + la.k[2 * st]);
-      hi = lds_b128<0>(kbase + la.k[2 * st + 1]);
+      lo = lds_b128<0>(kaddr<false>(k0, la, kbase, 2 * st));
+      hi = lds_b128<0>(kaddr<false>(k0, la, kbase, 2 * st + 1));
     } else {
-      lo = lds_b128<32 * 128>(kbase + la.k[2 * st]);
-      hi = lds_b128<32 * 128>(kbase + la.k[2 * st + 1]);
+      lo = lds_b128<32 * 128>(kaddr<false>(k0, la, kbase, 2 * st));
+      hi = lds_b128<32 * 128>(kaddr<false>(k0, la, kbase, 2 * st + 1));
     }
     ko[i] = u32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   }
@@ -360,8 +402,9 @@ template <int QB>
 __device__ __forceinline__ void pv_step8(unsigned vbase, const LaneAddr& la,
                                          const u32x8 (&pf)[QB], f32x16 (&o)[4][QB]) {
   u32x8 vo[2];
+  const unsigned v0 = lane_base<false>(vbase, la.v[0]);
   auto read_v = [&](int db, u32x8& dst) {
-    const unsigned a = vbase + la.v[db];
+    const unsigned a = vaddr<5, false>(v0, la, vbase, db);
     const u32x2 r0 = lds_tr8<0>(a), r1 = lds_tr8<16 * 128>(a), r2 = lds_tr8<32 * 128>(a),
                 r3 = lds_tr8<48 * 128>(a);
     dst = u32x8{r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
@@ -407,11 +450,12 @@ __device__ __forceinline__ void qk_step(unsigned kbase, const LaneAddr& la,
     for (int qb = 0; qb < QB; ++qb) s[kb][qb] = f32x16{};
   constexpr int KD = ATTN_KDEPTH < N ? ATTN_KDEPTH : N;
   u32x4 ko[KD];
+  const unsigned k0 = lane_base(kbase, la.k[0]);
   auto read_k = [&](int i, u32x4& dst) {
     // i = kb * DS + st (cases past N are never taken)
 #define ATTN_KREAD(I)                                                                  \
   case I:                                                                              \
-    dst = lds_b128<((I) / DS) * 32 * G::ROW>(kbase + la.k[(I) % DS]);                 \
+    dst = lds_b128<((I) / DS) * 32 * G::ROW>(kaddr(k0, la, kbase, (I) % DS));         \
     break;
     switch (i) {
       ATTN_KREAD(0) ATTN_KREAD(1) ATTN_KREAD(2) ATTN_KREAD(3) ATTN_KREAD(4) ATTN_KREAD(5)
@@ -657,15 +701,16 @@ __device__ __forceinline__ void pv_step(unsigned vbase, const LaneAddr& la,
   using G = Geom<HD>;
   constexpr int N = G::VOPS;
   u32x4 vo[4];
+  const unsigned v0 = lane_base(vbase, la.v[0]);
   auto read_v = [&](int i, u32x4& dst) {
     u32x2 lo, hi;
     // cases past N are never taken
 #define ATTN_VREAD(I)                                                                  \
   case I:                                                                              \
     lo = lds_tr16<(32 * (((I) >> 1) & 1) + 16 * ((I) & 1)) * G::ROW>(                  \
-        vbase + la.v[(I) >> 2]);                                                       \
+        vaddr<6>(v0, la, vbase, (I) >> 2));                                            \
     hi = lds_tr16<(32 * (((I) >> 1) & 1) + 16 * ((I) & 1) + 8) * G::ROW>(              \
-        vbase + la.v[(I) >> 2]);                                                       \
+        vaddr<6>(v0, la, vbase, (I) >> 2));                                            \
     break;
     switch (i) {
       ATTN_VREAD(0) ATTN_VREAD(1) ATTN_VREAD(2) ATTN_VREAD(3) ATTN_VREAD(4) ATTN_VREAD(5)
