@@ -49,18 +49,16 @@ enum MfmaOrder { PV_FIRST = 0, QK_FIRST = 1 };
 #ifndef ATTN_PERSIST
 #define ATTN_PERSIST 1
 #endif
-// Where an item's output is written (the next item's Q load and first K tile
-// are always issued together, under one wait).  EARLY: by each wave as soon as
-// its last P V product is done, in the softmax phase that follows; with the
-// causal mask the waves of a diagonal block finish their rows up to three
-// steps apart, so most stores complete while the others still compute.
-// DEFERRED: at the next item's start, after that item's Q and first K tile
-// are issued, so that the stores' latency overlaps the loads'.  Measured
-// (paired, against writing each item's output after its last step): EARLY
-// +1.8% causal bf16, +0.9% at S = 32768, +7.5% FP8, but -0.5% on the
-// non-causal fp16 workload, where DEFERRED gains 0.7%.  So causal and FP8
-// launches write early and the others deferred.
-enum EpiloguePlace { EPI_EARLY = 0, EPI_DEFERRED = 1 };
+// Each wave writes its rows' output as soon as its last P V product is done,
+// in the softmax phase that follows: with the causal mask the waves of a
+// diagonal block finish their rows up to three steps apart, so most stores
+// complete while the others still compute, and the next item's Q and first K
+// tile then wait on fewer stores.  Measured (paired, against writing the
+// output after the item's last step): +1.8% causal bf16, +0.9% at S = 32768,
+// +7.5% FP8, and +0.4% to +0.9% on non-causal shapes once the output goes out
+// through the LDS slice below (-0.5% before, when issuing the stores after
+// the next item's loads gained 0.7% there).
+
 
 // 1: Q in and the 16-bit O out through a per-wave LDS slice (whole rows per
 // memory instruction); 0: straight between HBM and the registers.
@@ -325,10 +323,6 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fa_fwd_kernel(
       }
     }
   };
-  const int epi_place = (causal || F::FP8) ? EPI_EARLY : EPI_DEFERRED;
-  // the item whose output is still to be written (EPI_DEFERRED)
-  bool pending = false;
-  int p_bh = 0, p_qw0 = 0, p_sp = 0;
 
   const int n_wg = (int)gridDim.x;
   for (int round = 0;; ++round) {
@@ -371,10 +365,8 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fa_fwd_kernel(
     }
 
     // Q^T operands of the wave's query n; rows past Sq read as zeros.  Waited
-    // for together with the first K tile (and the previous item's stores)
+    // for together with the first K tile (and this wave's last stores)
     typename F::QFrag qf;
-    // the previous item's output, if still to be written (it uses the slice)
-    if (pending) epilogue(p_bh, p_qw0, p_sp);
     if constexpr (F::STAGE_IO) {
       // the wave's 32 rows into its slice, whole rows per instruction
       const __amdgpu_buffer_rsrc_t qr =
@@ -586,11 +578,11 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fa_fwd_kernel(
       mfma_end();
       barrier();
       softmax_begin(j);
-      if (epi_place == EPI_EARLY) epilogue(bh, qw0, sp);
+      epilogue(bh, qw0, sp);
       softmax_end();
       barrier();
       ++j;
-    } else if (epi_place == EPI_EARLY) {
+    } else {
       epilogue(bh, qw0, sp);  // no key for this wave's rows (or no rows)
     }
     for (; j <= n_tiles; ++j) {  // steps with nothing left for this wave
@@ -603,14 +595,7 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fa_fwd_kernel(
     }
     if (group_a) barrier();
 
-    if (epi_place == EPI_DEFERRED) {
-      pending = true;
-      p_bh = bh;
-      p_qw0 = qw0;
-      p_sp = sp;
-    }
   }
-  if (pending) epilogue(p_bh, p_qw0, p_sp);
 }
 
 // Compute units of the device `stream` runs on (0 if unknown), cached per device.
