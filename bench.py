@@ -159,6 +159,38 @@ def hbm_read_ceiling(gib=4, iters=10):
     return best
 
 
+def decode_read_ceiling(iters=10):
+    """Read rate of the decode's memory side without its math
+    (csrc_bench/decode_read.hip) at the decode workload's geometry: one
+    single-wave workgroup per (batch, kv head, split), its K and V tiles through
+    direct-to-LDS loads one tile ahead.  Returns GB/s of K and V bytes with the
+    two arrays the decode reads, and with one contiguous array."""
+    import ctypes
+
+    lib = ctypes.CDLL(os.path.join(os.path.dirname(A.__file__), "libattn_bench.so"))
+    lib.decode_read.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.decode_read.restype = ctypes.c_int
+    wgs = DECODE.B * DECODE.Hkv * DECODE.num_splits
+    tiles = DECODE.Sk // DECODE.num_splits // 64
+    tile_bytes = 64 * DECODE.d * 2
+    assert DECODE.d == 128 and tiles * DECODE.num_splits * 64 == DECODE.Sk
+    half = wgs * tiles * tile_bytes
+    buf = torch.zeros(2 * half, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    out = {}
+    for one, name in ((0, "two_arrays"), (1, "one_array")):
+        def run():
+            if lib.decode_read(ctypes.c_void_p(buf.data_ptr()),
+                               ctypes.c_void_p(buf.data_ptr() + half), wgs, tiles, one,
+                               ctypes.c_void_p(sink.data_ptr()), stream) != 0:
+                raise RuntimeError("decode_read launch failed")
+        out[name] = round(2 * half / (_time_ms(run, iters) * 1e-3) / 1e9, 1)
+    del buf, sink
+    return out
+
+
 def other_workloads(iters=20):
     """Throughput of the other workloads (context; their parity is checked by the
     GPU tests): the other prefill shapes in TFLOP/s, and the headline prefill
@@ -449,6 +481,7 @@ def main():
         gemm = {}
         gemm_best = float("nan")
         stream_gbs, stream_shape = float("nan"), None
+        dec_read = {}
         others = {}
     else:
         gemm = {"bf16_8192^3": round(gemm_ceiling(torch.bfloat16), 1),
@@ -456,6 +489,7 @@ def main():
                 "bf16_bmm_32x8192x8192x128": round(bmm_ceiling(), 1)}
         gemm_best = max(gemm.values())
         stream_gbs, stream_shape = hbm_read_ceiling()
+        dec_read = decode_read_ceiling()
         others = other_workloads()
 
     traffic_pre, traffic_dec = measured_traffic()
@@ -490,11 +524,14 @@ def main():
                    "value": round(dec_gbs, 1), "unit": "GB/s",
                    "frac_hbm_peak": round(dec_gbs / PEAK_HBM_GBS, 4),
                    "frac_read_stream_ceiling": ratio(dec_gbs, stream_gbs),
+                   "frac_decode_read_ceiling": ratio(dec_gbs, dec_read.get("two_arrays",
+                                                                           float("nan"))),
                    "algorithmic_bytes": dec_bytes},
         "gemm_ceiling_tflops": gemm,
         "hbm_read_stream_ceiling": {"value": None if stream_shape is None else round(stream_gbs, 1),
                                     "unit": "GB/s",
                                     "shape": stream_shape, "bytes": 4 << 30},
+        "decode_read_ceiling": {"unit": "GB/s", **dec_read},
         "other_workloads": others,
         "warmup_run": warm,
         "gpu_state": {"before": state_before, "after": state_after},
