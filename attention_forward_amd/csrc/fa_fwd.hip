@@ -66,6 +66,10 @@ enum MfmaOrder { PV_FIRST = 0, QK_FIRST = 1 };
 #define ATTN_STAGE_IO 1
 #endif
 
+#ifndef ATTN_XCD_ORDER
+#define ATTN_XCD_ORDER 1
+#endif
+
 #ifndef ATTN_ORDER16
 #define ATTN_ORDER16 0
 #endif
@@ -325,17 +329,49 @@ __global__ __launch_bounds__(FWD_NW * 64, 2) void fa_fwd_kernel(
   };
 
   const int n_wg = (int)gridDim.x;
+  // XCD-grouped order.  Workgroup i runs on XCD i mod 8 (measured on the
+  // device), so the workgroups of an XCD share its L2.  Each XCD takes
+  // the kv heads u with u mod 8 = its index, and walks their items head by
+  // head (within a head, query blocks heaviest first, the query heads of a
+  // GQA group side by side), its workgroup c taking positions c, 2C - 1 - c,
+  // 2C + c, ... of that list (C workgroups per XCD).  So all of an XCD's
+  // compute units work on the same kv head at the same time and fetch its K/V
+  // tiles into one L2 about once, instead of once per round of the global
+  // order below; and, as there, a causal workgroup's heavy and light items
+  // pair up.  Used when the grid and the kv heads divide into the 8 XCDs,
+  // else the global order.
+  const int grp_q = Hq / Hkv;  // query heads per kv head
+  const int n_kvh = n_bh / grp_q;
+  const int C = n_wg >> 3;
+  const bool xcd_order =
+      ATTN_XCD_ORDER && !PART && (n_wg & 7) == 0 && C > 0 && (n_kvh & 7) == 0;
+  const int xcd = (int)blockIdx.x & 7, c_in = (int)blockIdx.x >> 3;
+  const int per_xcd = (n_kvh >> 3) * grp_q * n_qt;
   for (int round = 0;; ++round) {
-    const int item = round * n_wg + ((round & 1) ? n_wg - 1 - (int)blockIdx.x : (int)blockIdx.x);
-    if (item >= n_items) break;
-    const int sp = PART ? item % n_split : 0;
-    const int t = PART ? item / n_split : item;
-    const int rank = t / n_bh;
-    const int bh = t - rank * n_bh;
-    const int qt = causal ? (n_qt - 1 - rank) : rank;
+    int sp = 0, bh, qt;
+    if (xcd_order) {
+      const int p = round * C + ((round & 1) ? C - 1 - c_in : c_in);
+      if (p >= per_xcd) break;
+      const int ui = p / (grp_q * n_qt);
+      const int rem = p - ui * (grp_q * n_qt);
+      const int rank = rem / grp_q;
+      const int u = xcd + 8 * ui;  // kv head b * Hkv + hkv
+      const int bb = u / Hkv;
+      bh = bb * Hq + (u - bb * Hkv) * grp_q + (rem - rank * grp_q);
+      qt = causal ? (n_qt - 1 - rank) : rank;
+    } else {
+      const int item =
+          round * n_wg + ((round & 1) ? n_wg - 1 - (int)blockIdx.x : (int)blockIdx.x);
+      if (item >= n_items) break;
+      sp = PART ? item % n_split : 0;
+      const int t = PART ? item / n_split : item;
+      const int rank = t / n_bh;
+      bh = t - rank * n_bh;
+      qt = causal ? (n_qt - 1 - rank) : rank;
+    }
     const int b = bh / Hq;
     const int hq = bh - b * Hq;
-    const int hkv = hq / (Hq / Hkv);
+    const int hkv = hq / grp_q;
 
     // keys [kv0, kv0 + Sk) of the head, indexed from kv0 below
     const int kv0 = PART ? sp * split_keys : 0;
