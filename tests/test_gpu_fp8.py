@@ -101,6 +101,7 @@ FP8_SMALL = [
     (1, 3, 3, 129, 63, F16, True),
     (2, 4, 4, 640, 640, BF16, True),
     (1, 2, 1, 513, 1000, F16, False),
+    (1, 16, 8, 2200, 2200, BF16, True),  # more items than a 256-CU grid, XCD-grouped order
 ]
 
 

@@ -107,7 +107,21 @@ SMALL_D64 = [
 ]
 
 
-@pytest.mark.parametrize("shape", [s + (128,) for s in SMALL] + [s + (64,) for s in SMALL_D64],
+# More work items (kv heads x query tiles) than a 256-CU persistent grid, so
+# each workgroup takes several: grouped-query shapes whose kv heads divide
+# into the 8 XCDs (the XCD-grouped item order, with several kv heads per XCD
+# and batches > 1) and one whose kv heads do not (the global order).
+MANY_ITEMS = [
+    # B, Hq, Hkv, Sq, Sk, dtype, causal, d
+    (1, 16, 8, 2200, 2200, BF16, True, 128),
+    (2, 32, 8, 700, 700, F16, False, 128),
+    (1, 16, 8, 2200, 2200, F16, True, 64),
+    (1, 12, 4, 3000, 3000, BF16, True, 128),
+]
+
+
+@pytest.mark.parametrize("shape", [s + (128,) for s in SMALL] + [s + (64,) for s in SMALL_D64] +
+                         MANY_ITEMS,
                          ids=lambda s: "B%d_Hq%d_Hkv%d_Sq%d_Sk%d_%s_%s_d%d" % (
     s[0], s[1], s[2], s[3], s[4], "bf16" if s[5] else "f16", "causal" if s[6] else "full", s[7]))
 def test_small_shapes_all_rows(shape):
