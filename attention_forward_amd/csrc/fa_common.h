@@ -23,6 +23,8 @@
 namespace attn {
 
 constexpr int KT = 64;  // keys per K/V tile
+constexpr int LOG2_KT = 6;
+static_assert(KT == 1 << LOG2_KT, "tiles of a power-of-two key count");
 
 // Geometry of one head dimension HD (64 or 128): a K or V row is HD 16-bit
 // elements, read in 16-byte slots; a direct-to-LDS load instruction moves a
